@@ -1,0 +1,288 @@
+"""Benchmark of the Q4_0 matmul library on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input: for the
+headline workload (FFN-up decode GEMV, W 9728 x 2560 in Q4_0, x float32
+1 x 2560) that is one q4_0_matmul call.  Inputs are resident in HBM before
+the timed region.  Successive steps rotate through copies of the repacked
+weights totalling at least 1 GiB, so that the 256 MB Infinity Cache cannot
+serve them and the figure is HBM bandwidth.
+
+Prints ONE JSON line (rank 0, N = 1): effective weight GB/s (Q4_0 bytes, 18
+per 32 weights, over the per-step time measured with HIP events on the launch
+stream), the roofline object for the kernel that runs, the oracle's CPU
+baseline, and under "extra" the other workloads (small GEMV, batched decode
+of a 4B-class block, logit head, prefill GEMMs), each with its own roofline
+fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_0 matmul effective weight GB/s (n≤8) and TFLOP/s (n=512), % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFS = 2500.0     # MI355X dense fp16 MFMA
+ROTATE_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="ffn_up_decode",
+                    choices=["gemv_1024", "ffn_up_decode", "block_decode",
+                             "logit_head", "prefill"])
+    ap.add_argument("--n", type=int, default=None, help="rows of x (decode workloads)")
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "gemv_dpp", "gemv_mfma", "gemm"])
+    ap.add_argument("--quick", action="store_true",
+                    help="headline workload only (no extra workloads, no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_code(q4, name):
+    return {"auto": q4.KERNEL_AUTO, "gemv_dpp": q4.KERNEL_GEMV_DPP,
+            "gemv_mfma": q4.KERNEL_GEMV_MFMA, "gemm": q4.KERNEL_GEMM}[name]
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_q4_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Case:
+    """One linear: repacked copies of W, an x and a y on the device."""
+
+    def __init__(self, torch, q4, synth, out, in_, n, x_dtype, seed, copies):
+        self.out, self.in_, self.n = out, in_, n
+        blk = synth.make_blocks(out, in_, seed=seed)
+        b = torch.from_numpy(blk.reshape(-1)).cuda()
+        base = q4.repacked(b, out, in_)
+        del b
+        self.packed = [base] + [base.clone() for _ in range(copies - 1)]
+        npdt = np.float16 if x_dtype == "f16" else np.float32
+        self.x = torch.from_numpy(synth.make_x(n, in_, seed=seed + 1000, dtype=npdt)).cuda()
+        self.xcode = q4.F16 if x_dtype == "f16" else q4.F32
+        self.y = torch.empty((n, out), dtype=torch.float32, device="cuda")
+        self.wbytes = q4.q4_0_blocks_bytes(out, in_)
+        self.flops = 2.0 * n * out * in_
+
+
+def timed(torch, q4, cases, kernel, steps, warmup):
+    """Run `steps` steps (each step = every case once, on its next weight
+    copy) between two events on the launch stream; return ms per step."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ncopy = len(cases[0].packed)
+
+    def step(i):
+        for c in cases:
+            q4.q4_0_matmul_ex(c.packed[i % ncopy], c.x, c.xcode, c.y, c.n, c.out,
+                              c.in_, kernel, sh)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def copies_for(total_bytes):
+    return max(2, -(-ROTATE_BYTES // max(1, total_bytes)))
+
+
+def parity_check(q4, oracle, synth, case, seed, rows=64):
+    """Oracle check of the benched configuration on sampled rows."""
+    blk = synth.make_blocks(case.out, case.in_, seed=seed)
+    x = case.x.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    r = np.unique(rng.integers(0, case.out, size=rows))
+    y_ref, den = oracle.matmul(blk, x, case.out, case.in_, rows=r)
+    y = case.y.cpu().numpy()[:, r]
+    return oracle.max_ratio(y, y_ref, den)
+
+
+def traffic_for(workload, kernel_name):
+    """Counter-measured HBM bytes per launch, if taken on the current sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    ent = data.get(workload)
+    if not ent or ent.get("src_sha") != source_hash() or ent.get("kernel") != kernel_name:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup):
+    total_w = sum(q4.q4_0_blocks_bytes(o, i) for o, i in linears)
+    copies = copies_for(total_w)
+    cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies)
+             for k, (o, i) in enumerate(linears)]
+    ms = timed(torch, q4, cases, kernel, steps, warmup)
+    gbs = total_w / (ms * 1e-3) / 1e9
+    kern = sorted({q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, o, i) if kernel == 0 else kernel]
+                   for o, i in linears})
+    res = {"workload": name, "n": n, "ms_per_step": round(ms, 5),
+           "weight_bytes": total_w, "GB/s": round(gbs, 1),
+           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern,
+           "launches_per_step": len(linears), "rotation_copies": copies}
+    del cases
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_line(torch, q4, synth, kernel, steps, warmup):
+    res = []
+    for li, (o, i) in enumerate([(9728, 2560), (2560, 9728)]):
+        c = Case(torch, q4, synth, o, i, 512, "f16", seed=li, copies=4)
+        ms = timed(torch, q4, [c], kernel, steps, warmup)
+        tfs = c.flops / (ms * 1e-3) / 1e12
+        res.append({"linear": f"{o}x{i}", "n": 512, "ms_per_step": round(ms, 5),
+                    "TFLOP/s": round(tfs, 2), "frac_mfma_f16": round(tfs / F16_MFMA_PEAK_TFS, 4),
+                    "kernel": q4.KERNEL_NAMES[q4.q4_0_select_kernel(512, o, i, q4.F16)
+                                              if kernel == 0 else kernel]})
+        del c
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(oracle, synth, out, in_, n, seconds):
+    blk = synth.make_blocks(out, in_, seed=0)
+    x = synth.make_x(n, in_, seed=1000)
+    times, threads = [], 0
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        _, _, threads = oracle.matmul(blk, x, out, in_, return_threads=True)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end and len(times) >= 3:
+            break
+    t = float(np.median(times))
+    wbytes = out * (in_ // 32) * 18
+    return {"value": round(wbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(times)} full oracle passes of the {out}x{in_} n={n} workload "
+                      f"(median {t * 1e3:.1f} ms each, ~{sum(times):.0f} s total)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    import gemm_q4_amd as q4
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    kernel = kernel_code(q4, args.kernel)
+    wl = synth.WORKLOADS[args.workload]
+    n = args.n if args.n is not None else wl.ns[0]
+
+    if args.workload == "prefill":
+        lines = prefill_line(torch, q4, synth, kernel, args.steps, args.warmup)
+        head = lines[0]
+        value, unit, ms = head["TFLOP/s"], "TFLOP/s", head["ms_per_step"]
+        roof = {"bound": "mfma", "achieved": value, "peak": F16_MFMA_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(value / F16_MFMA_PEAK_TFS, 4),
+                "traffic": traffic_for(args.workload, head["kernel"])}
+        cfg = {"workload": "prefill", "linears": [l["linear"] for l in lines], "n": 512,
+               "x_dtype": "f16", "kernel": head["kernel"]}
+        dtype = "f16"
+        extra = {"prefill": lines}
+        parity = None
+    else:
+        linears = [(l.out, l.in_) for l in wl.linears]
+        total_w = sum(q4.q4_0_blocks_bytes(o, i) for o, i in linears)
+        copies = copies_for(total_w)
+        cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies)
+                 for k, (o, i) in enumerate(linears)]
+        ms = timed(torch, q4, cases, kernel, args.steps, args.warmup)
+        parity = max(parity_check(q4, __import__("oracle"), synth, c, seed=k)
+                     for k, c in enumerate(cases))
+        value = total_w / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+        kname = q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, *linears[0]) if kernel == 0 else kernel]
+        per_launch_bytes = total_w / len(linears)
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(args.workload, kname)}
+        cfg = {"workload": args.workload, "linears": [f"{o}x{i}" for o, i in linears],
+               "n": n, "x_dtype": "f32", "kernel": kname, "rotation_copies": copies,
+               "weight_bytes_per_step": total_w,
+               "algorithmic_bytes_per_launch": per_launch_bytes}
+        dtype = "f32"
+        del cases
+        torch.cuda.empty_cache()
+        extra = {}
+        if not args.quick:
+            extra["decode"] = []
+            extra["decode"].append(decode_line(torch, q4, synth, "gemv_1024", [(1024, 1024)], 1,
+                                               kernel, 2000, 100))
+            blk = [(l.out, l.in_) for l in synth.WORKLOADS["block_decode"].linears]
+            for nn in (1, 2, 4, 8):
+                extra["decode"].append(decode_line(torch, q4, synth, "block_decode", blk, nn,
+                                                   kernel, 300, 30))
+            for nn in (1, 4):
+                extra["decode"].append(decode_line(torch, q4, synth, "logit_head",
+                                                   [(151936, 2560)], nn, kernel, 200, 20))
+            extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": dtype, "data": "synthetic", "config": cfg, "roofline": roof}
+    if parity is not None:
+        rec["parity_max_ratio"] = parity
+    if not args.quick and not args.no_cpu_baseline:
+        import oracle
+        o, i = wl.linears[0].out, wl.linears[0].in_
+        rec["cpu_baseline"] = cpu_baseline(oracle, synth, o, i, n, args.cpu_seconds)
+    if extra:
+        rec["extra"] = extra
+    rec["source_sha"] = source_hash()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+"""Python binding of libq4_0, the MI355X Q4_0 matmul library (include/q4_0.h).
+
+Argument marshalling only: every function calls the C entry point of the same
+name in ``libq4_0.so`` (built in this directory by ``gemm_q4_amd.build``).
+Pointer arguments accept torch tensors (their ``data_ptr()``) or integers;
+``stream`` accepts a ``torch.cuda.Stream``, an integer hipStream_t, or None
+(torch's current stream on the tensors' device, else the null stream).
+A negative status raises ``Q4Error``.  There is no CPU fallback: importing
+this package fails if the HIP library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4_0.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# constants of include/q4_0.h
+OK, EINVAL, ESHAPE, ENULL, EALIGN, EALIAS, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+F32, F16 = 0, 1
+KERNEL_AUTO, KERNEL_GEMV_DPP, KERNEL_GEMV_MFMA, KERNEL_GEMM = 0, 1, 2, 3
+KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GEMV_DPP: "gemv_dpp",
+                KERNEL_GEMV_MFMA: "gemv_mfma", KERNEL_GEMM: "gemm"}
+MAX_IN, MAX_OUT, MAX_N = 1048576, 16777216, 65536
+
+_i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "q4_0_blocks_bytes": (_sz, [_i64, _i64]),
+    "q4_0_packed_bytes": (_sz, [_i64, _i64]),
+    "q4_0_repack": (_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q4_0_unpack": (_int, [_vp, _vp, _i64, _i64, _vp]),
+    "q4_0_matmul": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _vp]),
+    "q4_0_matmul_ex": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _vp]),
+    "q4_0_select_kernel": (_int, [_i64, _i64, _i64, _int]),
+    "q4_0_kernel_supports": (_int, [_int, _i64, _i64, _i64, _int]),
+    "q4_0_strerror": (ctypes.c_char_p, [_int]),
+    "q4_0_version": (_int, []),
+    "q4_0_release_workspaces": (_int, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {q4_0_strerror(status)} (status {status})")
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is None:
+        for t in tensors:
+            if hasattr(t, "is_cuda") and t.is_cuda:
+                import torch
+                return torch.cuda.current_stream(t.device).cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> int:
+    if status < 0:
+        raise Q4Error(status, where)
+    return status
+
+
+def q4_0_strerror(status: int) -> str:
+    return _lib.q4_0_strerror(status).decode()
+
+
+def q4_0_version() -> int:
+    return _lib.q4_0_version()
+
+
+def q4_0_blocks_bytes(out: int, in_: int) -> int:
+    return _lib.q4_0_blocks_bytes(out, in_)
+
+
+def q4_0_packed_bytes(out: int, in_: int) -> int:
+    return _lib.q4_0_packed_bytes(out, in_)
+
+
+def q4_0_repack(blocks, packed, out: int, in_: int, stream=None) -> None:
+    _check(_lib.q4_0_repack(_ptr(blocks), _ptr(packed), out, in_,
+                            _stream(stream, blocks, packed)), "q4_0_repack")
+
+
+def q4_0_unpack(packed, blocks, out: int, in_: int, stream=None) -> None:
+    _check(_lib.q4_0_unpack(_ptr(packed), _ptr(blocks), out, in_,
+                            _stream(stream, packed, blocks)), "q4_0_unpack")
+
+
+def q4_0_matmul(packed, x, x_dtype: int, y, n: int, out: int, in_: int,
+                stream=None) -> None:
+    _check(_lib.q4_0_matmul(_ptr(packed), _ptr(x), x_dtype, _ptr(y), n, out, in_,
+                            _stream(stream, packed, x, y)), "q4_0_matmul")
+
+
+def q4_0_matmul_ex(packed, x, x_dtype: int, y, n: int, out: int, in_: int,
+                   kernel: int, stream=None) -> None:
+    _check(_lib.q4_0_matmul_ex(_ptr(packed), _ptr(x), x_dtype, _ptr(y), n, out,
+                               in_, kernel, _stream(stream, packed, x, y)),
+           "q4_0_matmul_ex")
+
+
+def q4_0_select_kernel(n: int, out: int, in_: int, x_dtype: int = F32) -> int:
+    return _check(_lib.q4_0_select_kernel(n, out, in_, x_dtype), "q4_0_select_kernel")
+
+
+def q4_0_kernel_supports(kernel: int, n: int, out: int, in_: int,
+                         x_dtype: int = F32) -> bool:
+    st = _lib.q4_0_kernel_supports(kernel, n, out, in_, x_dtype)
+    if st == EUNSUPPORTED:
+        return False
+    _check(st, "q4_0_kernel_supports")
+    return True
+
+
+def q4_0_release_workspaces() -> None:
+    _check(_lib.q4_0_release_workspaces(), "q4_0_release_workspaces")
+
+
+# ---- torch conveniences (allocation through torch, then the C calls above) --
+def dtype_code(x) -> int:
+    """Q4_0_F32 or Q4_0_F16 for a torch tensor's dtype."""
+    import torch
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.float16:
+        return F16
+    raise TypeError(f"x must be float32 or float16, not {x.dtype}")
+
+
+def repacked(blocks, out: int, in_: int, stream=None):
+    """Repack a uint8 CUDA tensor of GGUF blocks into a new packed tensor."""
+    import torch
+    packed = torch.empty(q4_0_packed_bytes(out, in_), dtype=torch.uint8,
+                         device=blocks.device)
+    q4_0_repack(blocks, packed, out, in_, stream)
+    return packed
+
+
+def matmul(packed, x, out: int, y=None, kernel: int = KERNEL_AUTO, stream=None):
+    """y[n x out] = x . W^T for a 2-D CUDA tensor x (float32 or float16)."""
+    import torch
+    n, in_ = x.shape
+    if y is None:
+        y = torch.empty((n, out), dtype=torch.float32, device=x.device)
+    q4_0_matmul_ex(packed, x, dtype_code(x), y, n, out, in_, kernel, stream)
+    return y

@@ -1,0 +1,195 @@
+// C ABI of libq4_0 (declared in include/q4_0.h): argument checks, kernel
+// choice, launches.  Every check runs on the host before any HIP call, so an
+// invalid call enqueues nothing and is testable without a GPU.
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/q4_0.h"
+#include "q4_0_internal.h"
+
+namespace {
+
+// Workspaces for K-split kernels, one per (device, stream), allocated on first
+// use and zeroed on that stream, so that concurrent calls on different streams
+// never share partial sums or counters.
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, void *> g_ws;
+
+int get_workspace(hipStream_t stream, void **ws) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return Q4_0_EHIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    const auto key = std::make_pair(dev, (uintptr_t)stream);
+    auto it = g_ws.find(key);
+    if (it != g_ws.end()) {
+        *ws = it->second;
+        return Q4_0_OK;
+    }
+    void *p = nullptr;
+    if (hipMalloc(&p, q4::kWorkspaceBytes) != hipSuccess) return Q4_0_EHIP;
+    if (hipMemsetAsync(p, 0, q4::kWorkspaceBytes, stream) != hipSuccess) {
+        (void)hipFree(p);
+        return Q4_0_EHIP;
+    }
+    g_ws[key] = p;
+    *ws = p;
+    return Q4_0_OK;
+}
+
+int check_shape(int64_t n, int64_t out, int64_t in) {
+    if (n < 1 || n > Q4_0_MAX_N) return Q4_0_ESHAPE;
+    if (out < 1 || out > Q4_0_MAX_OUT) return Q4_0_ESHAPE;
+    if (in < 32 || in > Q4_0_MAX_IN || in % 32 != 0) return Q4_0_ESHAPE;
+    return Q4_0_OK;
+}
+
+bool overlaps(const void *a, size_t alen, const void *b, size_t blen) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + blen && b0 < a0 + alen;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t elem_bytes(int dtype) { return dtype == Q4_0_F16 ? 2 : 4; }
+
+bool supports(int kernel, int64_t n, int64_t out, int64_t in, int x_f16) {
+    switch (kernel) {
+    case Q4_0_KERNEL_GEMV_DPP: return q4::gemv_dpp_supports(n, out, in, x_f16);
+    case Q4_0_KERNEL_GEMV_MFMA: return q4::gemv_mfma_supports(n, out, in, x_f16);
+    case Q4_0_KERNEL_GEMM: return q4::gemm_supports(n, out, in, x_f16);
+    default: return false;
+    }
+}
+
+// The automatic choice (goinfer primer ch. 10, "Which kernel runs is a
+// runtime decision": pick what is fastest here, not merely what can run).
+int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
+    if (n <= 8) {
+        if (n == 1 && q4::gemv_dpp_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_DPP;
+        if (q4::gemv_mfma_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_MFMA;
+        if (q4::gemv_dpp_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_DPP;
+    }
+    return Q4_0_KERNEL_GEMM;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? Q4_0_OK : Q4_0_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t q4_0_blocks_bytes(int64_t out, int64_t in) {
+    if (check_shape(1, out, in) != Q4_0_OK) return 0;
+    return (size_t)out * (size_t)(in / 32) * 18u;
+}
+
+size_t q4_0_packed_bytes(int64_t out, int64_t in) {
+    if (check_shape(1, out, in) != Q4_0_OK) return 0;
+    return (size_t)q4::Layout(out, in).total_bytes();
+}
+
+int q4_0_repack(const void *blocks, void *packed, int64_t out, int64_t in, void *stream) {
+    const int st = check_shape(1, out, in);
+    if (st != Q4_0_OK) return st;
+    if (!blocks || !packed) return Q4_0_ENULL;
+    if (!aligned(packed, 16)) return Q4_0_EALIGN;
+    if (overlaps(blocks, q4_0_blocks_bytes(out, in), packed, q4_0_packed_bytes(out, in)))
+        return Q4_0_EALIAS;
+    return map_hip(q4::launch_repack(blocks, packed, out, in, (hipStream_t)stream));
+}
+
+int q4_0_unpack(const void *packed, void *blocks, int64_t out, int64_t in, void *stream) {
+    const int st = check_shape(1, out, in);
+    if (st != Q4_0_OK) return st;
+    if (!blocks || !packed) return Q4_0_ENULL;
+    if (!aligned(packed, 16)) return Q4_0_EALIGN;
+    if (overlaps(blocks, q4_0_blocks_bytes(out, in), packed, q4_0_packed_bytes(out, in)))
+        return Q4_0_EALIAS;
+    return map_hip(q4::launch_unpack(packed, blocks, out, in, (hipStream_t)stream));
+}
+
+int q4_0_kernel_supports(int kernel, int64_t n, int64_t out, int64_t in, int x_dtype) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    if (kernel == Q4_0_KERNEL_AUTO) return Q4_0_OK;
+    if (kernel < Q4_0_KERNEL_GEMV_DPP || kernel > Q4_0_KERNEL_GEMM) return Q4_0_EINVAL;
+    return supports(kernel, n, out, in, x_dtype == Q4_0_F16) ? Q4_0_OK : Q4_0_EUNSUPPORTED;
+}
+
+int q4_0_select_kernel(int64_t n, int64_t out, int64_t in, int x_dtype) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    return auto_kernel(n, out, in, x_dtype == Q4_0_F16);
+}
+
+int q4_0_matmul_ex(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
+                   int64_t out, int64_t in, int kernel, void *stream) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    if (kernel < Q4_0_KERNEL_AUTO || kernel > Q4_0_KERNEL_GEMM) return Q4_0_EINVAL;
+    if (!packed || !x || !y) return Q4_0_ENULL;
+    if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_0_EALIGN;
+    const size_t ybytes = (size_t)n * (size_t)out * 4u;
+    const size_t xbytes = (size_t)n * (size_t)in * (size_t)elem_bytes(x_dtype);
+    if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, packed, q4_0_packed_bytes(out, in)))
+        return Q4_0_EALIAS;
+    const int x_f16 = x_dtype == Q4_0_F16;
+    const int k = kernel == Q4_0_KERNEL_AUTO ? auto_kernel(n, out, in, x_f16) : kernel;
+    if (!supports(k, n, out, in, x_f16)) return Q4_0_EUNSUPPORTED;
+    const hipStream_t s = (hipStream_t)stream;
+    switch (k) {
+    case Q4_0_KERNEL_GEMV_DPP: return map_hip(q4::launch_gemv_dpp(packed, x, x_f16, y, n, out, in, s));
+    case Q4_0_KERNEL_GEMV_MFMA: {
+        void *ws = nullptr;
+        if (q4::gemv_mfma_workspace_bytes(n, out, in) > 0) {
+            const int wst = get_workspace(s, &ws);
+            if (wst != Q4_0_OK) return wst;
+        }
+        return map_hip(q4::launch_gemv_mfma(packed, x, x_f16, y, n, out, in, ws, s));
+    }
+    default: return map_hip(q4::launch_gemm(packed, x, x_f16, y, n, out, in, s));
+    }
+}
+
+int q4_0_matmul(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
+                int64_t out, int64_t in, void *stream) {
+    return q4_0_matmul_ex(packed, x, x_dtype, y, n, out, in, Q4_0_KERNEL_AUTO, stream);
+}
+
+const char *q4_0_strerror(int status) {
+    switch (status) {
+    case Q4_0_OK: return "success";
+    case Q4_0_EINVAL: return "invalid dtype or kernel selector";
+    case Q4_0_ESHAPE: return "invalid shape (need n, out >= 1, in >= 32, in % 32 == 0, within limits)";
+    case Q4_0_ENULL: return "null pointer argument";
+    case Q4_0_EALIGN: return "misaligned pointer (packed and x need 16 bytes, y 4 bytes)";
+    case Q4_0_EALIAS: return "output buffer overlaps an input buffer";
+    case Q4_0_EUNSUPPORTED: return "the requested kernel cannot take this shape";
+    case Q4_0_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+int q4_0_version(void) { return 100; }
+
+int q4_0_release_workspaces(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    int dev0 = 0;
+    if (hipGetDevice(&dev0) != hipSuccess) return Q4_0_EHIP;
+    int st = Q4_0_OK;
+    for (auto &kv : g_ws) {
+        if (hipSetDevice(kv.first.first) != hipSuccess ||
+            hipStreamSynchronize((hipStream_t)kv.first.second) != hipSuccess ||
+            hipFree(kv.second) != hipSuccess)
+            st = Q4_0_EHIP;
+    }
+    g_ws.clear();
+    if (hipSetDevice(dev0) != hipSuccess) st = Q4_0_EHIP;
+    return st;
+}
+
+}  // extern "C"

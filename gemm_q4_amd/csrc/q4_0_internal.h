@@ -1,0 +1,50 @@
+// Internal declarations shared by the kernel files and the C-ABI front end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4_0_layout.h"
+
+namespace q4 {
+
+// Grid size for a grid-stride loop over `total` items: enough blocks to fill
+// the device many times over, capped so the dispatch stays far below the
+// 32-bit work-item limit.
+inline int64_t grid_for(int64_t total, int block) {
+    int64_t g = (total + block - 1) / block;
+    const int64_t cap = 1 << 16;
+    return g < 1 ? 1 : (g > cap ? cap : g);
+}
+
+// Workspace for kernels that split K across workgroups: per-slice partial
+// sums plus one arrival counter per tile run.  Counters are zero between
+// calls (the last workgroup of a run resets its counter).
+constexpr size_t kWorkspaceBytes = size_t(8) << 20;
+inline size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
+
+hipError_t launch_repack(const void *blocks, void *packed, int64_t out, int64_t in,
+                         hipStream_t stream);
+hipError_t launch_unpack(const void *packed, void *blocks, int64_t out, int64_t in,
+                         hipStream_t stream);
+
+// Small-n VALU kernel: x staged in LDS as float32, one 16-row tile pair per
+// workgroup, four waves splitting K, DPP/shuffle reduction across lanes.
+bool gemv_dpp_supports(int64_t n, int64_t out, int64_t in, int x_f16);
+hipError_t launch_gemv_dpp(const void *packed, const void *x, int x_f16, float *y,
+                           int64_t n, int64_t out, int64_t in, hipStream_t stream);
+
+// Small-n MFMA kernel: activations split into binary16 high and low parts
+// (a 16-row MFMA A operand), weights decoded to exact q - 8 in binary16.
+bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16);
+size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in);
+hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y,
+                            int64_t n, int64_t out, int64_t in, void *ws,
+                            hipStream_t stream);
+
+// Prefill kernel: binary16 MFMA on d * (q - 8) rounded to binary16.
+bool gemm_supports(int64_t n, int64_t out, int64_t in, int x_f16);
+hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y,
+                       int64_t n, int64_t out, int64_t in, hipStream_t stream);
+
+}  // namespace q4

@@ -1,0 +1,152 @@
+/*
+ * libq4_0: GGUF Q4_0 block-quantized weight matmul on one AMD MI355X (gfx950).
+ *
+ *     y[n x out] = x[n x in] . W^T,   W[out x in] in Q4_0 blocks.
+ *
+ * W is stored the way rembed's matmul interface stores a linear layer's
+ * weight (rembed "Architecture", "The pluggable kernel interface"): [out x in]
+ * row-major, so each output is the dot product of a weight row with an
+ * activation row.  Each row is cut into groups of 32 weights along `in`
+ * (goinfer primer ch. 10, "Making Go fast enough": groups of 32, a scale plus
+ * small integers two to a byte).  A GGUF Q4_0 block is 18 bytes: the group's
+ * scale d as IEEE binary16, little-endian, then 16 code bytes in the
+ * split-half order of goinfer ch. 10 "Layout, concretely" (byte i: weight i in
+ * the low four bits, weight i+16 in the high four bits).  Weight = d * (q - 8).
+ *
+ * Conventions for every entry point:
+ *  - Pointers to weights, activations and outputs are DEVICE pointers owned by
+ *    the caller.  The library never synchronizes the host with the device
+ *    and enqueues its work only on `stream` (a hipStream_t; NULL is the null
+ *    stream of the current device).  The current HIP device must be the one
+ *    holding the buffers.
+ *  - Device memory: shapes whose K is split across workgroups (long rows,
+ *    few row tiles) need a small workspace for partial sums.  q4_0_matmul
+ *    allocates it (8 MiB, hipMalloc) the first time such a shape runs on a
+ *    (device, stream) pair, zeroes it on that stream, and keeps it for later
+ *    calls on that pair until q4_0_release_workspaces.  Run one call per
+ *    stream before capturing that stream into a graph.  Nothing else is
+ *    allocated.
+ *  - Arguments are validated on the host before any HIP call; an invalid
+ *    call returns a negative Q4_0_E* status and enqueues nothing.  Launch
+ *    failures return Q4_0_EHIP.  Errors of work already enqueued (for
+ *    example a fault) surface on the stream, as for any HIP kernel.
+ *  - No silent fallback: a kernel forced with q4_0_matmul_ex that cannot
+ *    take the shape returns Q4_0_EUNSUPPORTED; it never runs another kernel.
+ *  - Stateless and thread-safe; calls on different streams may overlap.
+ */
+#ifndef Q4_0_H
+#define Q4_0_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (0 = success). */
+#define Q4_0_OK 0
+#define Q4_0_EINVAL (-1)       /* unknown dtype or kernel selector            */
+#define Q4_0_ESHAPE (-2)       /* n/out/in <= 0, in % 32 != 0, or too large   */
+#define Q4_0_ENULL (-3)        /* a required pointer is NULL                  */
+#define Q4_0_EALIGN (-4)       /* a pointer is not aligned as required        */
+#define Q4_0_EALIAS (-5)       /* an output overlaps an input                 */
+#define Q4_0_EUNSUPPORTED (-6) /* forced kernel cannot take this shape        */
+#define Q4_0_EHIP (-7)         /* the HIP runtime rejected a launch           */
+
+/* Activation element types. */
+#define Q4_0_F32 0             /* float32 x                                   */
+#define Q4_0_F16 1             /* IEEE binary16 x                             */
+
+/* Kernel selectors for q4_0_matmul_ex. */
+#define Q4_0_KERNEL_AUTO 0      /* what q4_0_matmul runs                      */
+#define Q4_0_KERNEL_GEMV_DPP 1  /* small n: VALU dot, x in LDS, DPP/shuffle
+                                   reduction; n <= 8                          */
+#define Q4_0_KERNEL_GEMV_MFMA 2 /* small n: fp16 MFMA on split activations;
+                                   n <= 8                                     */
+#define Q4_0_KERNEL_GEMM 3      /* prefill: tiles dequantized to fp16, MFMA   */
+
+/* Largest sizes accepted (32-bit grid and index limits). */
+#define Q4_0_MAX_IN 1048576
+#define Q4_0_MAX_OUT 16777216
+#define Q4_0_MAX_N 65536
+
+/* Bytes of an [out x in] matrix in GGUF Q4_0 blocks: out * (in/32) * 18.
+ * Returns 0 for an invalid shape. */
+size_t q4_0_blocks_bytes(int64_t out, int64_t in);
+
+/* Bytes of the repacked matrix: the GGUF size with out rounded up to a
+ * multiple of 16 (the repacked matrix is cut into 16-row tiles; padding rows
+ * decode to zero).  Equal to q4_0_blocks_bytes when out % 16 == 0.
+ * Returns 0 for an invalid shape. */
+size_t q4_0_packed_bytes(int64_t out, int64_t in);
+
+/* One-time repack of GGUF Q4_0 blocks into the kernels' layout: goinfer ch. 10
+ * "Making Go fast enough" (quantized weights rearranged once so the kernel
+ * reads them in order) and "Layout, concretely".  The split-half order inside
+ * a block is kept; scales and codes go to two separate streams, each read
+ * with wide coalesced loads.  Same size as the input (no second copy is kept
+ * alongside it, unlike the opt-in repack that section prices at +80%).
+ *   blocks : [out][in/32] GGUF blocks, q4_0_blocks_bytes(out,in) bytes,
+ *            any alignment.
+ *   packed : q4_0_packed_bytes(out,in) bytes, 16-byte aligned, must not
+ *            overlap `blocks` (Q4_0_EALIAS).  Fully overwritten.
+ * The bytes are moved unchanged: q4_0_unpack restores `blocks` bit for bit,
+ * NaN and Inf scales included.  The caller may free `blocks` once the stream
+ * has passed this call. */
+int q4_0_repack(const void *blocks, void *packed, int64_t out, int64_t in,
+                void *stream);
+
+/* Inverse of q4_0_repack: writes the q4_0_blocks_bytes(out,in) GGUF bytes
+ * (padding rows are dropped).  Same alignment and overlap rules. */
+int q4_0_unpack(const void *packed, void *blocks, int64_t out, int64_t in,
+                void *stream);
+
+/* y = x . W^T with W repacked by q4_0_repack.  The two workloads are the
+ * goinfer primer ch. 10 "What the kernels are" pair: the memory-bound decode
+ * product (few activation rows, the weights read once for all of them, as in
+ * golem's continuous batching, golem README "Several conversations, one
+ * pass") and the prefill product (hundreds of rows, compute-bound).
+ *   packed : repacked W, 16-byte aligned.
+ *   x      : [n x in] row-major, element type x_dtype (Q4_0_F32 or
+ *            Q4_0_F16), 16-byte aligned.
+ *   y      : [n x out] row-major float32, 4-byte aligned, fully overwritten,
+ *            must not overlap `packed` or `x`.
+ *   n, out, in : 1 <= n <= Q4_0_MAX_N, 1 <= out <= Q4_0_MAX_OUT,
+ *            32 <= in <= Q4_0_MAX_IN, in % 32 == 0.
+ * Accuracy, as max |y - y_exact| / sum_k |w x| over outputs: <= 1e-3 on the
+ * small-n kernels (float32 accumulation), <= 1e-2 on the prefill kernel
+ * (binary16 operands; float32 activations are rounded to binary16 there). */
+int q4_0_matmul(const void *packed, const void *x, int x_dtype, float *y,
+                int64_t n, int64_t out, int64_t in, void *stream);
+
+/* q4_0_matmul with the kernel chosen by the caller (tests, benchmarks).
+ * Q4_0_KERNEL_AUTO behaves exactly as q4_0_matmul. */
+int q4_0_matmul_ex(const void *packed, const void *x, int x_dtype, float *y,
+                   int64_t n, int64_t out, int64_t in, int kernel,
+                   void *stream);
+
+/* The kernel q4_0_matmul would run for this call shape (a Q4_0_KERNEL_*
+ * value), or a negative status for an invalid shape.  Host only. */
+int q4_0_select_kernel(int64_t n, int64_t out, int64_t in, int x_dtype);
+
+/* Whether `kernel` can take this shape: Q4_0_OK, Q4_0_EUNSUPPORTED, or
+ * another negative status for an invalid shape or selector.  Host only. */
+int q4_0_kernel_supports(int kernel, int64_t n, int64_t out, int64_t in,
+                         int x_dtype);
+
+/* Static text for a status code. */
+const char *q4_0_strerror(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int q4_0_version(void);
+
+/* Waits for each stream that owns a workspace, then frees every workspace
+ * q4_0_matmul allocated.  Returns Q4_0_OK or Q4_0_EHIP. */
+int q4_0_release_workspaces(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_0_H */

@@ -1,0 +1,160 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/q4_0.h declares, and rejects every invalid call before touching HIP.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_q4_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4_0.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_0_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for must in ("q4_0_repack", "q4_0_unpack", "q4_0_matmul", "q4_0_packed_bytes"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(q4.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+    assert sorted(q4.EXPORTED) == declared_functions()
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define Q4_0_([A-Z_0-9]+) \(?(-?\d+)\)?", text))
+    assert consts["OK"] == q4.OK and consts["EINVAL"] == q4.EINVAL
+    assert consts["ESHAPE"] == q4.ESHAPE and consts["ENULL"] == q4.ENULL
+    assert consts["EALIGN"] == q4.EALIGN and consts["EALIAS"] == q4.EALIAS
+    assert consts["EUNSUPPORTED"] == q4.EUNSUPPORTED and consts["EHIP"] == q4.EHIP
+    assert consts["F32"] == q4.F32 and consts["F16"] == q4.F16
+    assert consts["KERNEL_AUTO"] == q4.KERNEL_AUTO
+    assert consts["KERNEL_GEMV_DPP"] == q4.KERNEL_GEMV_DPP
+    assert consts["KERNEL_GEMV_MFMA"] == q4.KERNEL_GEMV_MFMA
+    assert consts["KERNEL_GEMM"] == q4.KERNEL_GEMM
+    assert consts["MAX_IN"] == q4.MAX_IN and consts["MAX_OUT"] == q4.MAX_OUT
+    assert consts["MAX_N"] == q4.MAX_N
+
+
+@pytest.mark.parametrize("out,in_", [(1024, 1024), (9728, 2560), (151936, 2560),
+                                     (2560, 9728), (1, 32), (17, 96), (100, 4128)])
+def test_sizes(out, in_):
+    nb = in_ // 32
+    assert q4.q4_0_blocks_bytes(out, in_) == out * nb * 18
+    tiles = (out + 15) // 16
+    groups = (nb + 3) // 4
+    assert q4.q4_0_packed_bytes(out, in_) == tiles * 16 * groups * 4 * 18
+    if out % 16 == 0 and in_ % 128 == 0:
+        assert q4.q4_0_packed_bytes(out, in_) == q4.q4_0_blocks_bytes(out, in_)
+
+
+def test_head_block_bytes_match_the_quoted_size():
+    # a 151936 x 2560 Q4_0 head is 218,787,840 bytes (18 bytes per 32 weights)
+    assert q4.q4_0_blocks_bytes(151936, 2560) == 218_787_840
+
+
+@pytest.mark.parametrize("out,in_", [(0, 32), (-1, 32), (10, 0), (10, 31), (10, 33),
+                                     (10, 16), (q4.MAX_OUT + 1, 32), (1, q4.MAX_IN + 32)])
+def test_invalid_shapes_have_no_size(out, in_):
+    assert q4.q4_0_blocks_bytes(out, in_) == 0
+    assert q4.q4_0_packed_bytes(out, in_) == 0
+
+
+A16 = 1 << 20      # fake, 16-byte aligned "device" addresses: never dereferenced
+B16 = 1 << 30
+C16 = 1 << 34
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except q4.Q4Error as e:
+        return e.status
+    return q4.OK
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, B16, q4.F32, C16, 0, 10, 64), q4.ESHAPE),
+    ((A16, B16, q4.F32, C16, 1, 0, 64), q4.ESHAPE),
+    ((A16, B16, q4.F32, C16, 1, 10, 48), q4.ESHAPE),
+    ((A16, B16, q4.F32, C16, q4.MAX_N + 1, 10, 64), q4.ESHAPE),
+    ((A16, B16, 7, C16, 1, 10, 64), q4.EINVAL),
+    ((0, B16, q4.F32, C16, 1, 10, 64), q4.ENULL),
+    ((A16, 0, q4.F32, C16, 1, 10, 64), q4.ENULL),
+    ((A16, B16, q4.F32, 0, 1, 10, 64), q4.ENULL),
+    ((A16 + 8, B16, q4.F32, C16, 1, 10, 64), q4.EALIGN),
+    ((A16, B16 + 4, q4.F32, C16, 1, 10, 64), q4.EALIGN),
+    ((A16, B16, q4.F32, C16 + 2, 1, 10, 64), q4.EALIGN),
+    ((A16, B16, q4.F32, B16 + 64, 1, 10, 64), q4.EALIAS),    # y inside x
+    ((A16, B16, q4.F32, A16 + 16, 1, 10, 64), q4.EALIAS),    # y inside W
+])
+def test_matmul_validation(args, expect):
+    assert status_of(q4.q4_0_matmul, *args, 0) == expect
+
+
+def test_matmul_ex_rejects_bad_kernel_and_unsupported_shapes():
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, 9, 0) == q4.EINVAL
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, -1, 0) == q4.EINVAL
+    # small-n kernels take n <= 8 only
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 9, 10, 64,
+                     q4.KERNEL_GEMV_DPP, 0) == q4.EUNSUPPORTED
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 9, 10, 64,
+                     q4.KERNEL_GEMV_MFMA, 0) == q4.EUNSUPPORTED
+    # the LDS-staged kernel cannot hold 8 rows of a 16384-wide x
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 8, 10, 16384,
+                     q4.KERNEL_GEMV_DPP, 0) == q4.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", [q4.q4_0_repack, q4.q4_0_unpack])
+def test_repack_validation(fn):
+    assert status_of(fn, A16, B16, 10, 48, 0) == q4.ESHAPE
+    assert status_of(fn, 0, B16, 10, 64, 0) == q4.ENULL
+    assert status_of(fn, A16, 0, 10, 64, 0) == q4.ENULL
+    src, dst = (A16, B16 + 8) if fn is q4.q4_0_repack else (A16 + 8, B16)
+    assert status_of(fn, src, dst, 10, 64, 0) == q4.EALIGN
+    assert status_of(fn, A16, A16 + 32, 10, 64, 0) == q4.EALIAS
+
+
+def test_kernel_choice_table():
+    """What the automatic choice runs for the workloads' shapes."""
+    sel = q4.q4_0_select_kernel
+    assert sel(1, 9728, 2560) in (q4.KERNEL_GEMV_DPP, q4.KERNEL_GEMV_MFMA)
+    for n in (2, 4, 8):
+        for out, in_ in [(4096, 2560), (1024, 2560), (2560, 4096), (9728, 2560),
+                         (2560, 9728), (151936, 2560)]:
+            assert sel(n, out, in_) in (q4.KERNEL_GEMV_DPP, q4.KERNEL_GEMV_MFMA)
+    assert sel(512, 9728, 2560, q4.F16) == q4.KERNEL_GEMM
+    assert sel(512, 2560, 9728, q4.F16) == q4.KERNEL_GEMM
+    assert sel(9, 100, 64) == q4.KERNEL_GEMM
+    with pytest.raises(q4.Q4Error):
+        sel(0, 10, 64)
+    with pytest.raises(q4.Q4Error):
+        sel(1, 10, 64, 5)
+
+
+def test_kernel_supports():
+    assert q4.q4_0_kernel_supports(q4.KERNEL_GEMM, 512, 9728, 2560, q4.F16)
+    assert q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 8, 2560, 9728)
+    assert not q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 9, 2560, 9728)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_0_kernel_supports(17, 1, 10, 64)
+
+
+def test_strerror_covers_every_status():
+    for st in (q4.OK, q4.EINVAL, q4.ESHAPE, q4.ENULL, q4.EALIGN, q4.EALIAS,
+               q4.EUNSUPPORTED, q4.EHIP):
+        assert q4.q4_0_strerror(st) != "unknown status"
+    assert q4.q4_0_strerror(-99) == "unknown status"
+    assert q4.q4_0_version() >= 100

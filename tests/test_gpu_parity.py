@@ -1,0 +1,256 @@
+"""GPU parity: every kernel of libq4_0 against the CPU oracle, through the C ABI.
+
+Bar: max |y - y_ref| / sum|w x| <= 1e-3 for the small-n kernels (float32
+accumulation) and <= 1e-2 for the prefill kernel (binary16 operands); the
+repack round trip is bit exact.  Inputs are the seeded synthetic workloads of
+``synth`` (d ~ U[0.001, 0.01] in binary16, codes ~ U{0..15}, x ~ N(0, 1)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemm_q4_amd as q4
+import oracle
+import synth
+from gpu_util import (DEV, TOL_GEMM, TOL_SMALL_N, packed_from_blocks, ratio, run,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_N_KERNELS = [q4.KERNEL_GEMV_DPP, q4.KERNEL_GEMV_MFMA]
+
+
+def _supported(kernel, n, out, in_, x_dtype=q4.F32):
+    return q4.q4_0_kernel_supports(kernel, n, out, in_, x_dtype)
+
+
+# ------------------------------------------------------------------ repack
+@pytest.mark.parametrize("out,in_", [(1, 32), (17, 96), (16, 128), (37, 4128),
+                                     (1024, 1024), (9728, 2560)])
+def test_repack_roundtrip_bit_exact_random_bytes(out, in_):
+    rng = np.random.default_rng(out * 7 + in_)
+    raw = rng.integers(0, 256, size=synth.blocks_bytes(out, in_), dtype=np.uint8)
+    # plant every special binary16 scale pattern: NaNs, infinities, -0,
+    # subnormals, max normal
+    specials = [0x7E00, 0x7C01, 0x7FFF, 0x7C00, 0xFC00, 0x8000, 0x0001, 0x03FF, 0x7BFF, 0xFE00]
+    blk = raw.reshape(out, in_ // 32, 18)
+    for i, s in enumerate(specials):
+        blk.reshape(-1, 18)[i % blk.reshape(-1, 18).shape[0], 0:2] = [s & 0xFF, s >> 8]
+    b = to_dev(raw)
+    p = q4.repacked(b, out, in_)
+    back = torch.empty_like(b)
+    q4.q4_0_unpack(p, back, out, in_)
+    torch.cuda.synchronize()
+    assert p.numel() == q4.q4_0_packed_bytes(out, in_)
+    assert torch.equal(back.cpu(), torch.from_numpy(raw))
+
+
+def test_repack_is_deterministic_and_size_preserving():
+    out, in_ = 4096, 2560
+    blk = synth.make_blocks(out, in_, seed=5)
+    p1 = packed_from_blocks(blk, out, in_)
+    p2 = packed_from_blocks(blk, out, in_)
+    assert torch.equal(p1, p2)
+    assert p1.numel() == blk.size                 # out % 16 == 0, in % 128 == 0
+
+
+# ------------------------------------------------------------------ small n
+SMALL_SHAPES = [(1024, 1024), (37, 96), (300, 160), (16, 32), (1, 4128), (513, 2592)]
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("out,in_", SMALL_SHAPES)
+def test_small_n_parity(kernel, n, out, in_):
+    if not _supported(kernel, n, out, in_):
+        pytest.skip("shape outside this kernel's range")
+    blk = synth.make_blocks(out, in_, seed=out + in_)
+    x = synth.make_x(n, in_, seed=n)
+    y = run(packed_from_blocks(blk, out, in_), x, out, kernel)
+    assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+def test_small_n_ffn_up_decode(kernel):
+    out, in_ = 9728, 2560
+    blk = synth.make_blocks(out, in_, seed=0)
+    x = synth.make_x(1, in_, seed=0)
+    y = run(packed_from_blocks(blk, out, in_), x, out, kernel)
+    assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_block_decode_all_linears_auto(n):
+    wl = synth.WORKLOADS["block_decode"]
+    for i, lin in enumerate(wl.linears):
+        blk = synth.make_blocks(lin.out, lin.in_, seed=synth.seed_for(wl.name, i))
+        x = synth.make_x(n, lin.in_, seed=100 + i)
+        y = run(packed_from_blocks(blk, lin.out, lin.in_), x, lin.out)
+        r = ratio(y, blk, x, lin.out, lin.in_)
+        assert r <= TOL_SMALL_N, (lin.name, n, r)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_logit_head_full(n):
+    out, in_ = 151936, 2560
+    blk = synth.make_blocks(out, in_, seed=0)
+    x = synth.make_x(n, in_, seed=0)
+    y = run(packed_from_blocks(blk, out, in_), x, out)
+    assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+def test_small_n_f16_activations(kernel):
+    out, in_, n = 1000, 1056, 3
+    blk = synth.make_blocks(out, in_, seed=9)
+    x = synth.make_x(n, in_, seed=9, dtype=np.float16)
+    y = run(packed_from_blocks(blk, out, in_), x, out, kernel)
+    assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+@pytest.mark.parametrize("xscale", [1e-6, 1e-3, 3e2, 1e5])
+def test_small_n_activation_range(kernel, xscale):
+    """Tiny and huge activations: the MFMA kernel's power-of-two rescaling
+    keeps binary16 parts in range; the VALU kernel is float32 throughout."""
+    out, in_, n = 200, 640, 2
+    blk = synth.make_blocks(out, in_, seed=13)
+    x = (synth.make_x(n, in_, seed=13).astype(np.float64) * xscale).astype(np.float32)
+    y = run(packed_from_blocks(blk, out, in_), x, out, kernel)
+    assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+def test_small_n_one_hot_recovers_columns_exactly(kernel):
+    """x = e_k gives column k of d*(q-8) exactly (one nonzero product)."""
+    out, in_ = 48, 96
+    blk = synth.make_blocks(out, in_, seed=17)
+    ks = [0, 1, 15, 16, 31, 32, 47, 95]
+    x = np.zeros((len(ks), in_), np.float32)
+    for t, k in enumerate(ks):
+        x[t, k] = 1.0
+    y = run(packed_from_blocks(blk, out, in_), x, out, kernel)
+    w = oracle.dequantize(blk, out, in_)
+    for t, k in enumerate(ks):
+        assert np.array_equal(y[t], w[:, k]), k
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+def test_small_n_zero_cases_exact(kernel):
+    out, in_ = 64, 256
+    blk = synth.make_blocks(out, in_, seed=19)
+    p = packed_from_blocks(blk, out, in_)
+    y = run(p, np.zeros((3, in_), np.float32), out, kernel)
+    assert np.all(y == 0)
+    blk8 = blk.copy()
+    blk8[..., 2:] = 0x88
+    y = run(packed_from_blocks(blk8, out, in_), synth.make_x(2, in_, seed=1), out, kernel)
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
+def test_small_n_batch_invariance(kernel):
+    out, in_ = 2560, 4096
+    if not _supported(kernel, 8, out, in_):
+        pytest.skip("shape outside this kernel's range")
+    blk = synth.make_blocks(out, in_, seed=23)
+    x = synth.make_x(8, in_, seed=23)
+    p = packed_from_blocks(blk, out, in_)
+    y8 = run(p, x, out, kernel)
+    y_ref, den = oracle.matmul(blk, x, out, in_)
+    for t in (0, 3, 7):
+        y1 = run(p, x[t:t + 1], out, kernel)
+        assert oracle.max_ratio(y1[0], y_ref[t], den[t]) <= TOL_SMALL_N
+        assert oracle.max_ratio(y8[t], y_ref[t], den[t]) <= TOL_SMALL_N
+
+
+def test_k_split_path_is_deterministic():
+    """down projection (in = 9728) splits K across workgroups; the last
+    workgroup adds the slices in a fixed order, so repeated calls agree bit
+    for bit."""
+    out, in_, n = 2560, 9728, 8
+    blk = synth.make_blocks(out, in_, seed=29)
+    x = synth.make_x(n, in_, seed=29)
+    p = packed_from_blocks(blk, out, in_)
+    ys = [run(p, x, out, q4.KERNEL_GEMV_MFMA) for _ in range(3)]
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[1], ys[2])
+    assert ratio(ys[0], blk, x, out, in_) <= TOL_SMALL_N
+
+
+def test_auto_matches_forced_kernel_bitwise():
+    out, in_ = 1024, 2560
+    blk = synth.make_blocks(out, in_, seed=31)
+    p = packed_from_blocks(blk, out, in_)
+    for n in (1, 2, 8, 100):
+        x = synth.make_x(n, in_, seed=n)
+        k = q4.q4_0_select_kernel(n, out, in_)
+        assert np.array_equal(run(p, x, out), run(p, x, out, k))
+
+
+def test_runs_on_a_side_stream():
+    out, in_ = 4096, 2560
+    blk = synth.make_blocks(out, in_, seed=37)
+    x = synth.make_x(4, in_, seed=37)
+    p = packed_from_blocks(blk, out, in_)
+    s = torch.cuda.Stream()
+    xd = to_dev(x)
+    with torch.cuda.stream(s):
+        y = q4.matmul(p, xd, out)
+    s.synchronize()
+    assert ratio(y.cpu().numpy(), blk, x, out, in_) <= TOL_SMALL_N
+
+
+# ------------------------------------------------------------------ prefill
+@pytest.mark.parametrize("n,out,in_", [(9, 100, 96), (64, 256, 128), (100, 300, 160),
+                                       (130, 1000, 1056), (512, 1024, 1024)])
+@pytest.mark.parametrize("xdt", [np.float16, np.float32], ids=["xf16", "xf32"])
+def test_gemm_parity_small(n, out, in_, xdt):
+    blk = synth.make_blocks(out, in_, seed=n + out)
+    x = synth.make_x(n, in_, seed=n, dtype=xdt)
+    y = run(packed_from_blocks(blk, out, in_), x, out, q4.KERNEL_GEMM)
+    assert ratio(y, blk, x, out, in_) <= TOL_GEMM
+
+
+@pytest.mark.parametrize("li", [0, 1], ids=["up", "down"])
+def test_prefill_full_size_sampled_rows(li):
+    """The prefill passes at full size (512 positions), in the launch
+    configuration the benchmark times; the oracle checks 96 sampled weight
+    rows (all 512 positions each) plus the first and last rows."""
+    wl = synth.WORKLOADS["prefill"]
+    lin = wl.linears[li]
+    blk = synth.make_blocks(lin.out, lin.in_, seed=synth.seed_for(wl.name, li))
+    x = synth.make_x(512, lin.in_, seed=li, dtype=np.float16)
+    assert q4.q4_0_select_kernel(512, lin.out, lin.in_, q4.F16) == q4.KERNEL_GEMM
+    y = run(packed_from_blocks(blk, lin.out, lin.in_), x, lin.out)
+    rng = np.random.default_rng(li)
+    rows = np.unique(np.concatenate([[0, lin.out - 1],
+                                     rng.integers(0, lin.out, size=96)]))
+    assert ratio(y, blk, x, lin.out, lin.in_, rows=rows) <= TOL_GEMM
+
+
+def test_gemm_one_hot_within_binary16_rounding():
+    """x = e_k recovers column k of d*(q-8) up to one binary16 rounding."""
+    out, in_ = 256, 128
+    blk = synth.make_blocks(out, in_, seed=41)
+    x = np.zeros((16, in_), np.float16)
+    ks = list(range(0, 128, 8))
+    for t, k in enumerate(ks):
+        x[t, k] = 1.0
+    y = run(packed_from_blocks(blk, out, in_), x, out, q4.KERNEL_GEMM)
+    w = oracle.dequantize(blk, out, in_)
+    for t, k in enumerate(ks):
+        assert np.array_equal(y[t], w[:, k].astype(np.float16).astype(np.float32))
+
+
+# ------------------------------------------------------------------ errors
+def test_forced_kernel_that_cannot_take_the_shape_is_an_error():
+    out, in_ = 256, 9728 * 4
+    assert not q4.q4_0_kernel_supports(q4.KERNEL_GEMV_DPP, 8, out, in_)
+    p = torch.empty(q4.q4_0_packed_bytes(out, in_), dtype=torch.uint8, device=DEV)
+    x = torch.zeros((8, in_), dtype=torch.float32, device=DEV)
+    with pytest.raises(q4.Q4Error) as e:
+        q4.matmul(p, x, out, kernel=q4.KERNEL_GEMV_DPP)
+    assert e.value.status == q4.EUNSUPPORTED
+    with pytest.raises(q4.Q4Error):
+        q4.matmul(p, torch.zeros((9, in_), dtype=torch.float32, device=DEV), out,
+                  kernel=q4.KERNEL_GEMV_MFMA)
