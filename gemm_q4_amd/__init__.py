@@ -7,11 +7,19 @@ Pointer arguments accept torch tensors (their ``data_ptr()``) or integers;
 (torch's current stream on the tensors' device, else the null stream).
 A negative status raises ``Q4Error``.  There is no CPU fallback: importing
 this package fails if the HIP library has not been built.
+
+torch is imported before the library is loaded: torch ships its own HIP
+runtime under the same soname, and loading ours first would put two HIP
+runtimes in one process, whose streams and contexts do not mix.  With torch
+loaded first, libq4_0.so binds to torch's runtime; the import checks that
+only one copy of the HIP runtime is mapped.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+
+import torch  # noqa: F401  (must precede the CDLL below)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4_0.so")
@@ -22,6 +30,28 @@ if not os.path.exists(LIB_PATH):
         "(python -c 'import __graft_entry__ as g; g.build()')")
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _mapped_runtimes():
+    paths = {}
+    try:
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                parts = line.split()
+                if len(parts) >= 6:
+                    base = os.path.basename(parts[5])
+                    for lib in ("libamdhip64.so",):
+                        if base.startswith(lib):
+                            paths.setdefault(lib, set()).add(os.path.realpath(parts[5]))
+    except OSError:
+        pass
+    return paths
+
+
+for _libname, _paths in _mapped_runtimes().items():
+    if len(_paths) > 1:
+        raise ImportError(f"two copies of {_libname} are loaded ({sorted(_paths)}); "
+                          "import torch before anything that loads a HIP runtime")
 
 # constants of include/q4_0.h
 OK, EINVAL, ESHAPE, ENULL, EALIGN, EALIAS, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7

@@ -11,8 +11,7 @@
 namespace {
 
 // Workspaces for K-split kernels, one per (device, stream), allocated on first
-// use and zeroed on that stream, so that concurrent calls on different streams
-// never share partial sums or counters.
+// use, so that concurrent calls on different streams never share partial sums.
 std::mutex g_ws_mu;
 std::map<std::pair<int, uintptr_t>, void *> g_ws;
 
@@ -28,10 +27,6 @@ int get_workspace(hipStream_t stream, void **ws) {
     }
     void *p = nullptr;
     if (hipMalloc(&p, q4::kWorkspaceBytes) != hipSuccess) return Q4_0_EHIP;
-    if (hipMemsetAsync(p, 0, q4::kWorkspaceBytes, stream) != hipSuccess) {
-        (void)hipFree(p);
-        return Q4_0_EHIP;
-    }
     g_ws[key] = p;
     *ws = p;
     return Q4_0_OK;

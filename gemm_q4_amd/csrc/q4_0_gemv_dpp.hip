@@ -5,8 +5,8 @@
 // the way golem's passes carry several conversations through one read of the
 // weights (golem README, "Several conversations, one pass").
 //
-// Work split.  A workgroup of four waves owns TQ consecutive 16-row tiles and
-// all of K; wave w takes the 4-block groups j = w, w+4, ...  Lane l = g*16+r
+// Work split.  A workgroup of four waves owns TQ (1 or 2) consecutive 16-row
+// tiles and all of K; wave w takes the 4-block groups j = w, w+4, ...  Lane l = g*16+r
 // reads, per tile and group, the 16-byte word holding code bytes 4g..4g+3 of
 // row r for four blocks (one coalesced 1 KB chunk per wave) and 8 bytes of
 // row r's scales.  x is staged once per workgroup in LDS as float32; lanes
@@ -26,6 +26,15 @@ namespace q4 {
 constexpr int kDppThreads = 256;
 constexpr int kDppWaves = kDppThreads / 64;
 constexpr int64_t kDppMaxLds = 64 * 1024;
+
+__device__ __forceinline__ float4 load_f4(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+}
+__device__ __forceinline__ float4 load_f4(const _Float16 *p) {
+    const u2_t a = *reinterpret_cast<const u2_t *>(p);
+    const h2_t a0 = as_h2(a[0]), a1 = as_h2(a[1]);
+    return float4{(float)a0.x, (float)a0.y, (float)a1.x, (float)a1.y};
+}
 
 template <int NT, int TQ>
 __device__ __forceinline__ void dpp_block(const float *__restrict__ xs, int in, int b, int g,
@@ -65,6 +74,10 @@ template <int NT, int TQ, typename XT>
 __global__ __launch_bounds__(kDppThreads) void gemv_dpp_kernel(
     const uint8_t *__restrict__ packed, const XT *__restrict__ x, float *__restrict__ y,
     int64_t out, int64_t in64) {
+    // Groups a wave handles per batch; the batch's code and scale words are
+    // loaded before the previous batch is computed (the first batch before
+    // x is staged), so memory latency overlaps the staging and the math.
+    constexpr int CH = TQ >= 4 ? 2 : 4;
     extern __shared__ float smem[];
     const Layout L(out, in64);
     const int in = (int)in64;
@@ -72,16 +85,43 @@ __global__ __launch_bounds__(kDppThreads) void gemv_dpp_kernel(
     float *xs = smem;                    // [NT][inp], zero past in
     float *red = smem + NT * inp;        // [waves][TQ][NT][16]
     const int tid = threadIdx.x;
-
-    for (int i = tid; i < NT * inp; i += kDppThreads) {
-        const int t = i / inp, k = i - t * inp;
-        xs[i] = k < in ? to_f32(x[(int64_t)t * in + k]) : 0.0f;
-    }
-    __syncthreads();
-
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int64_t tile0 = (int64_t)blockIdx.x * TQ;
+    const int ng = (int)L.g4;
+
+    u4_t cw[CH][TQ], cwn[CH][TQ];
+    u2_t sw[CH][TQ], swn[CH][TQ];
+    // batch c0 covers the wave's groups j = wave + 4*(c0 + c), c < CH
+    auto load_batch = [&](int c0, u4_t (&c)[CH][TQ], u2_t (&sc)[CH][TQ]) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int j = wave + kDppWaves * (c0 + k);
+#pragma unroll
+            for (int i = 0; i < TQ; ++i) {
+                const int64_t t = tile0 + i;
+                if (j < ng && t < L.tiles) {
+                    c[k][i] = load_u4(packed + L.tile_codes(t) + (int64_t)j * kGroupCodeBytes + lane * 16);
+                    sc[k][i] = load_u2(packed + L.tile_scales(t) + (int64_t)j * kGroupScaleBytes + r * 8);
+                } else {
+                    c[k][i] = u4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+                    sc[k][i] = u2_t{0u, 0u};
+                }
+            }
+        }
+    };
+    load_batch(0, cw, sw);
+
+    // x rows staged as float32, four values per thread and step
+    const int inp4 = inp / 4, in4 = in / 4;
+#pragma unroll 4
+    for (int i = tid; i < NT * inp4; i += kDppThreads) {
+        const int t = i / inp4, k4 = i - t * inp4;
+        float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (k4 < in4) v = load_f4(x + (int64_t)t * in + 4 * k4);
+        *reinterpret_cast<float4 *>(xs + t * inp + 4 * k4) = v;
+    }
+    __syncthreads();
 
     float acc[TQ][NT];
 #pragma unroll
@@ -89,30 +129,32 @@ __global__ __launch_bounds__(kDppThreads) void gemv_dpp_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[i][t] = 0.0f;
 
-    for (int j = wave; j < (int)L.g4; j += kDppWaves) {
-        u4_t cw[TQ];
-        u2_t sw[TQ];
+    const int nmine = ng > wave ? (ng - wave + kDppWaves - 1) / kDppWaves : 0;
+    for (int c0 = 0; c0 < nmine; c0 += CH) {
+        const bool more = c0 + CH < nmine;
+        if (more) load_batch(c0 + CH, cwn, swn);
 #pragma unroll
-        for (int i = 0; i < TQ; ++i) {
-            const int64_t t = tile0 + i;
-            if (t < L.tiles) {
-                cw[i] = load_u4(packed + L.tile_codes(t) + (int64_t)j * kGroupCodeBytes + lane * 16);
-                sw[i] = load_u2(packed + L.tile_scales(t) + (int64_t)j * kGroupScaleBytes + r * 8);
-            } else {
-                cw[i] = u4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-                sw[i] = u2_t{0u, 0u};
+        for (int k = 0; k < CH; ++k) {
+            const int j = wave + kDppWaves * (c0 + k);
+            if (j < ng) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    uint32_t word[TQ];
+                    float d[TQ];
+#pragma unroll
+                    for (int i = 0; i < TQ; ++i) {
+                        word[i] = cw[k][i][s];
+                        d[i] = half_bits_to_float((sw[k][i][s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+                    }
+                    dpp_block<NT, TQ>(xs, inp, 4 * j + s, g, word, d, acc);
+                }
             }
         }
+        if (more) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint32_t word[TQ];
-            float d[TQ];
+            for (int k = 0; k < CH; ++k)
 #pragma unroll
-            for (int i = 0; i < TQ; ++i) {
-                word[i] = cw[i][s];
-                d[i] = half_bits_to_float((sw[i][s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
-            }
-            dpp_block<NT, TQ>(xs, inp, 4 * j + s, g, word, d, acc);
+                for (int i = 0; i < TQ; ++i) { cw[k][i] = cwn[k][i]; sw[k][i] = swn[k][i]; }
         }
     }
 
@@ -151,7 +193,7 @@ static int64_t dpp_lds_bytes(int64_t n, int64_t in, int tq) {
     return (n * L.g4 * kGroupBlocks * kBlockK + (int64_t)kDppWaves * tq * n * 16) * 4;
 }
 
-static int dpp_tq(int64_t n) { return n <= 2 ? 4 : 2; }
+static int dpp_tq(int64_t n) { return n <= 2 ? 2 : 1; }
 
 bool gemv_dpp_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     (void)out; (void)x_f16;
@@ -173,14 +215,14 @@ template <typename XT>
 static hipError_t launch_dpp_x(const void *packed, const void *x, float *y, int64_t n,
                                int64_t out, int64_t in, hipStream_t stream) {
     switch (n) {
-    case 1: return launch_dpp_t<1, 4, XT>(packed, x, y, out, in, stream);
-    case 2: return launch_dpp_t<2, 4, XT>(packed, x, y, out, in, stream);
-    case 3: return launch_dpp_t<3, 2, XT>(packed, x, y, out, in, stream);
-    case 4: return launch_dpp_t<4, 2, XT>(packed, x, y, out, in, stream);
-    case 5: return launch_dpp_t<5, 2, XT>(packed, x, y, out, in, stream);
-    case 6: return launch_dpp_t<6, 2, XT>(packed, x, y, out, in, stream);
-    case 7: return launch_dpp_t<7, 2, XT>(packed, x, y, out, in, stream);
-    case 8: return launch_dpp_t<8, 2, XT>(packed, x, y, out, in, stream);
+    case 1: return launch_dpp_t<1, 2, XT>(packed, x, y, out, in, stream);
+    case 2: return launch_dpp_t<2, 2, XT>(packed, x, y, out, in, stream);
+    case 3: return launch_dpp_t<3, 1, XT>(packed, x, y, out, in, stream);
+    case 4: return launch_dpp_t<4, 1, XT>(packed, x, y, out, in, stream);
+    case 5: return launch_dpp_t<5, 1, XT>(packed, x, y, out, in, stream);
+    case 6: return launch_dpp_t<6, 1, XT>(packed, x, y, out, in, stream);
+    case 7: return launch_dpp_t<7, 1, XT>(packed, x, y, out, in, stream);
+    case 8: return launch_dpp_t<8, 1, XT>(packed, x, y, out, in, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -18,10 +18,9 @@ inline int64_t grid_for(int64_t total, int block) {
 }
 
 // Workspace for kernels that split K across workgroups: per-slice partial
-// sums plus one arrival counter per tile run.  Counters are zero between
-// calls (the last workgroup of a run resets its counter).
-constexpr size_t kWorkspaceBytes = size_t(8) << 20;
-inline size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
+// sums, written by the product kernel and read by the reduction kernel that
+// follows it on the same stream.
+constexpr size_t kWorkspaceBytes = size_t(32) << 20;
 
 hipError_t launch_repack(const void *blocks, void *packed, int64_t out, int64_t in,
                          hipStream_t stream);

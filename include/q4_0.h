@@ -19,10 +19,11 @@
  *    and enqueues its work only on `stream` (a hipStream_t; NULL is the null
  *    stream of the current device).  The current HIP device must be the one
  *    holding the buffers.
- *  - Device memory: shapes whose K is split across workgroups (long rows,
- *    few row tiles) need a small workspace for partial sums.  q4_0_matmul
- *    allocates it (8 MiB, hipMalloc) the first time such a shape runs on a
- *    (device, stream) pair, zeroes it on that stream, and keeps it for later
+ *  - Device memory: shapes whose K is split across workgroups (on the
+ *    small-n MFMA kernel, when n * in is too large for one workgroup's LDS)
+ *    need a workspace for partial sums.  q4_0_matmul allocates it (32 MiB,
+ *    hipMalloc) the first
+ *    time such a shape runs on a (device, stream) pair and keeps it for later
  *    calls on that pair until q4_0_release_workspaces.  Run one call per
  *    stream before capturing that stream into a graph.  Nothing else is
  *    allocated.

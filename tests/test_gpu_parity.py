@@ -254,3 +254,49 @@ def test_forced_kernel_that_cannot_take_the_shape_is_an_error():
     with pytest.raises(q4.Q4Error):
         q4.matmul(p, torch.zeros((9, in_), dtype=torch.float32, device=DEV), out,
                   kernel=q4.KERNEL_GEMV_MFMA)
+
+
+def test_k_split_workspace_shared_across_shapes():
+    """Calls of different K-split shapes on one stream share one workspace;
+    each call finds its arrival counters at zero and leaves them at zero."""
+    shapes = [(300, 160, 1), (1024, 1024, 5), (2560, 9728, 8), (300, 160, 1), (64, 2560, 3)]
+    for out, in_, n in shapes:
+        blk = synth.make_blocks(out, in_, seed=out)
+        x = synth.make_x(n, in_, seed=in_)
+        y = run(packed_from_blocks(blk, out, in_), x, out, q4.KERNEL_GEMV_MFMA)
+        assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N, (out, in_, n)
+
+
+@pytest.mark.parametrize("kernel,n,out,in_,xdt", [
+    (q4.KERNEL_GEMV_DPP, 1, 1024, 2560, np.float32),
+    (q4.KERNEL_GEMV_MFMA, 4, 2560, 9728, np.float32),     # K split + reduction kernel
+    (q4.KERNEL_GEMM, 96, 512, 1024, np.float16),
+])
+def test_graph_replay_matches_eager(kernel, n, out, in_, xdt):
+    """Captured into a HIP graph, the library's launches replay to the eager
+    result, replay after replay, with eager work and syncs in between."""
+    blk = synth.make_blocks(out, in_, seed=43)
+    x = to_dev(synth.make_x(n, in_, seed=43, dtype=xdt))
+    p = packed_from_blocks(blk, out, in_)
+    y_eager = q4.matmul(p, x, out, kernel=kernel)
+    torch.cuda.synchronize()
+    ref = y_eager.clone()
+    y = torch.zeros_like(ref)
+    # the library keeps a workspace per stream: run once on the capture
+    # stream before capturing, as include/q4_0.h asks
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        q4.matmul(p, x, out, y=y, kernel=kernel)
+    cs.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        q4.matmul(p, x, out, y=y, kernel=kernel)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        other = q4.matmul(p, x, out, kernel=kernel)      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), rep
+        assert torch.equal(other, ref)
