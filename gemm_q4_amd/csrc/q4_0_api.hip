@@ -59,9 +59,11 @@ bool supports(int kernel, int64_t n, int64_t out, int64_t in, int x_f16) {
 
 // The automatic choice (goinfer primer ch. 10, "Which kernel runs is a
 // runtime decision": pick what is fastest here, not merely what can run).
+// Measured on MI355X for n <= 8 over the decode shapes (1024..151936 rows,
+// 1024..9728 columns): the MFMA kernel is as fast as or faster than the VALU
+// kernel everywhere, so it is first; the VALU kernel takes what it cannot.
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (n <= 8) {
-        if (n == 1 && q4::gemv_dpp_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_DPP;
         if (q4::gemv_mfma_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_MFMA;
         if (q4::gemv_dpp_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_DPP;
     }
