@@ -29,35 +29,51 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
+// The two magic words, held in vector registers.  gfx950's three-operand
+// (VOP3) encoding takes no literal and at most one scalar operand, so with both
+// the nibble mask and the magic as constants the compiler splits the masked
+// insert into an AND and an OR.  An identity quad-permutation move hides the
+// magic's value from constant folding; the insert then becomes one
+// v_and_or_b32 (mask from a scalar register, magic from this vector register).
+struct Magic {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ Magic pinned_magic() {
+    Magic m;
+    m.lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)kMagicLo, 0xE4, 0xF, 0xF, true);
+    m.hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)kMagicHi, 0xE4, 0xF, 0xF, true);
+    return m;
+}
+
 // Decode one 4-byte code word (code bytes 4g..4g+3 of a block) into the eight
 // exact values q - 8 as binary16, in the order
 //   k = 4g+0, 4g+1, 4g+2, 4g+3, 4g+16, 4g+17, 4g+18, 4g+19.
 // Byte i carries weight 4g+i in its low nibble and 4g+16+i in its high
 // nibble (split-half order).  v_perm spreads bytes 0,1 (then 2,3) into the
-// two 16-bit halves; one v_and_or per pair inserts the nibbles under the magic
-// exponents; one v_pk_add_f16 per pair removes the offset.
-__device__ __forceinline__ void decode_word(uint32_t w, uint32_t q[4]) {
+// two 16-bit halves; one masked insert per pair puts the nibbles under the
+// magic exponents; one v_pk_add_f16 per pair removes the offset.
+__device__ __forceinline__ void decode_word(uint32_t w, const Magic &m, uint32_t q[4]) {
     const uint32_t t01 = __builtin_amdgcn_perm(w, w, 0x0C010C00u);  // B0,0,B1,0
     const uint32_t t23 = __builtin_amdgcn_perm(w, w, 0x0C030C02u);  // B2,0,B3,0
     const h2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    q[0] = as_u32(as_h2((t01 & kMaskLo) | kMagicLo) + off_lo);
-    q[1] = as_u32(as_h2((t23 & kMaskLo) | kMagicLo) + off_lo);
-    q[2] = as_u32(as_h2((t01 & kMaskHi) | kMagicHi) + off_hi);
-    q[3] = as_u32(as_h2((t23 & kMaskHi) | kMagicHi) + off_hi);
+    q[0] = as_u32(as_h2((t01 & kMaskLo) | m.lo) + off_lo);
+    q[1] = as_u32(as_h2((t23 & kMaskLo) | m.lo) + off_lo);
+    q[2] = as_u32(as_h2((t01 & kMaskHi) | m.hi) + off_hi);
+    q[3] = as_u32(as_h2((t23 & kMaskHi) | m.hi) + off_hi);
 }
 
 // Same eight values in a cheaper order (one shift, no v_perm):
 //   k = 4g+0, 4g+2, 4g+16, 4g+18, 4g+1, 4g+3, 4g+17, 4g+19.
-// Used where the consumer picks its activation operands per value (VALU dot).
-__device__ __forceinline__ void decode_word_pairs(uint32_t w, uint32_t q[4]) {
+// Used where the consumer lays its activation operands out to match.
+__device__ __forceinline__ void decode_word_pairs(uint32_t w, const Magic &m, uint32_t q[4]) {
     const uint32_t w8 = w >> 8;
     const h2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    q[0] = as_u32(as_h2((w & kMaskLo) | kMagicLo) + off_lo);
-    q[1] = as_u32(as_h2((w & kMaskHi) | kMagicHi) + off_hi);
-    q[2] = as_u32(as_h2((w8 & kMaskLo) | kMagicLo) + off_lo);
-    q[3] = as_u32(as_h2((w8 & kMaskHi) | kMagicHi) + off_hi);
+    q[0] = as_u32(as_h2((w & kMaskLo) | m.lo) + off_lo);
+    q[1] = as_u32(as_h2((w & kMaskHi) | m.hi) + off_hi);
+    q[2] = as_u32(as_h2((w8 & kMaskLo) | m.lo) + off_lo);
+    q[3] = as_u32(as_h2((w8 & kMaskHi) | m.hi) + off_hi);
 }
 
 __device__ __forceinline__ h8_t pack_h8(const uint32_t q[4]) {

@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
     const Layout L(out, in);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const Magic mg = pinned_magic();
     const int g = lane >> 4, r = lane & 15;
     const int64_t m0 = (int64_t)blockIdx.y * kGemmBM;
     const int64_t tile0 = (int64_t)blockIdx.x * (kGemmBN / kTileRows) + wave * kGemmTilesPerWave;
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
 #pragma unroll
             for (int ni = 0; ni < kGemmTilesPerWave; ++ni) {
                 uint32_t q[4];
-                decode_word(cw[ni][s], q);
+                decode_word(cw[ni][s], mg, q);
                 const uint32_t dbits = (sw[ni][s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
                 const h2_t d2 = as_h2(dbits | (dbits << 16));
 #pragma unroll

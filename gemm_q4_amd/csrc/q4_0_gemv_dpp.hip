@@ -39,7 +39,7 @@ __device__ __forceinline__ float4 load_f4(const _Float16 *p) {
 template <int NT, int TQ>
 __device__ __forceinline__ void dpp_block(const float *__restrict__ xs, int in, int b, int g,
                                           const uint32_t (&word)[TQ], const float (&d)[TQ],
-                                          float (&acc)[TQ][NT]) {
+                                          const Magic &mg, float (&acc)[TQ][NT]) {
     // x values this lane needs: k = 32b + 4g + {0,1,2,3} and 32b + 16 + 4g + {0..3}
     float xv[NT][8];
 #pragma unroll
@@ -52,7 +52,7 @@ __device__ __forceinline__ void dpp_block(const float *__restrict__ xs, int in, 
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
         uint32_t q[4];
-        decode_word_pairs(word[i], q);
+        decode_word_pairs(word[i], mg, q);
         // q pairs hold k offsets (0,2), (16,18), (1,3), (17,19) -> x slots
         const h2_t q0 = as_h2(q[0]), q1 = as_h2(q[1]), q2 = as_h2(q[2]), q3 = as_h2(q[3]);
 #pragma unroll
@@ -86,6 +86,7 @@ __global__ __launch_bounds__(kDppThreads) void gemv_dpp_kernel(
     float *red = smem + NT * inp;        // [waves][TQ][NT][16]
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const Magic mg = pinned_magic();
     const int g = lane >> 4, r = lane & 15;
     const int64_t tile0 = (int64_t)blockIdx.x * TQ;
     const int ng = (int)L.g4;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kDppThreads) void gemv_dpp_kernel(
                         word[i] = cw[k][i][s];
                         d[i] = half_bits_to_float((sw[k][i][s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
                     }
-                    dpp_block<NT, TQ>(xs, inp, 4 * j + s, g, word, d, acc);
+                    dpp_block<NT, TQ>(xs, inp, 4 * j + s, g, word, d, mg, acc);
                 }
             }
         }

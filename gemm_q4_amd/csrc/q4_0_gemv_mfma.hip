@@ -24,11 +24,16 @@
 // hi and lo slots of a row are summed with one cross-lane shuffle (xor 32).
 //
 // Work split.  Workgroup (cx, sy) owns a run of 16-row tiles and the sy-th of
-// S slices of K; its waves take contiguous runs of at most GPW 4-block groups
-// of the slice, every tile of the run.  Each wave requests all of its code and
-// scale words of a tile at once, and the next tile's words before it computes
-// the current one.  Per tile the waves' partials meet in LDS and are summed in
-// a fixed order.  K is split (S > 1) only when the slice's A fragments would
+// S slices of K; its waves take contiguous runs of `per` <= GPW 4-block groups
+// of the slice, every tile of the run.  Order of requests: the workgroup's x
+// first (small, shared by every workgroup, so it comes from L2), then all of
+// the first tile's code and scale words, each wave's loads unconditionally
+// (a wave with fewer than GPW groups repeats its first address), so that the
+// memory counter lets every consumer wait for exactly its own words: x is
+// staged while the weights are still in flight, and block b's product waits
+// only for block b's word.  Each later tile's words are requested before the
+// current tile is computed.  Per tile the waves' partials meet in LDS and are
+// summed in a fixed order.  K is split (S > 1) only when the slice's A fragments would
 // not fit the LDS budget; then each workgroup parks its per-tile sums in a
 // workspace and a second small kernel adds the S slices in slice order.  The
 // kernel boundary orders the two, so no device-wide fence or atomic is needed
@@ -49,6 +54,8 @@ constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
 // x items (8 values) a thread stages: budget / 32 bytes per item / 256 threads
 constexpr int kMaxItems = (int)(Q4_MFMA_LDS_BUDGET / 32 / 256);
+// groups per wave a kernel instance holds in registers
+constexpr int kGpwSet[] = {2, 4, 5, 8, 10, 16};
 
 // 2^e with e clamped to the float32 normal range.
 __device__ __forceinline__ float pow2f(int e) {
@@ -66,9 +73,24 @@ template <> __device__ __forceinline__ float4 load_x4<_Float16>(const _Float16 *
     return float4{(float)a0.x, (float)a0.y, (float)a1.x, (float)a1.y};
 }
 
+// Everything the kernel needs, computed on the host (no division on device).
+struct MfmaArgs {
+    const uint8_t *packed;
+    const void *x;
+    float *y;
+    float *part;         // per-slice partial sums when S > 1
+    int64_t code_base;   // byte offset of the code stream in `packed`
+    int out, in;
+    int g4, tiles;       // groups per padded row, 16-row tiles
+    int gps;             // groups per K slice
+    int per;             // groups per wave (<= GPW)
+    int tpw;             // tiles per workgroup
+};
+
 struct MfmaPlan {
     int waves;        // waves per workgroup
-    int gpw;          // groups per wave (at most, template bound)
+    int gpw;          // register capacity per wave (template bound), >= per
+    int per;          // groups per wave
     int64_t gps;      // groups per K slice
     int64_t slices;   // S: workgroups along K
     int64_t tpw;      // tiles per workgroup
@@ -81,62 +103,33 @@ struct MfmaPlan {
 // the row's scaled values at k = 32*bl + 4g + {0, 2, 16, 18, 1, 3, 17, 19}
 // (the slot order of decode_word_pairs).
 template <int NT, typename XT, int GPW>
-__global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(
-    const uint8_t *__restrict__ packed, const XT *__restrict__ x, float *__restrict__ y,
-    int64_t out, int64_t in, int64_t gps, int64_t tiles_per_wg, float *__restrict__ part) {
+__global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const MfmaArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ float red[2][kMfmaMaxWaves][8][16];
     __shared__ float rowmax[kMfmaMaxWaves][8];
-    const Layout L(out, in);
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int nwaves = blockDim.x >> 6;
     const int g = lane >> 4, r = lane & 15;
-    const int64_t slices = gridDim.y;
-    const int64_t sy = blockIdx.y;
-    const int64_t gs0 = sy * gps;                            // first group of the slice
-    const int64_t gs1 = gs0 + gps < L.g4 ? gs0 + gps : L.g4;
-    const int nbs = (int)(gs1 - gs0) * 4;                    // blocks in the slice
-    // this wave's groups of the slice: [q0, q1)
-    const int per = (int)((gs1 - gs0 + nwaves - 1) / nwaves);
-    const int q0 = wave * per;
-    const int q1 = q0 + per < (int)(gs1 - gs0) ? q0 + per : (int)(gs1 - gs0);
-    const int ng = q1 > q0 ? q1 - q0 : 0;
+    const int sy = blockIdx.y;
+    const int gs0 = sy * a.gps;                              // first group of the slice
+    const int gsn = a.g4 - gs0 < a.gps ? a.g4 - gs0 : a.gps;  // groups in the slice
+    const int nbs = gsn * 4;                                 // blocks in the slice
+    // this wave's groups of the slice: [q0, q0 + ng)
+    const int q0 = wave * a.per;
+    const int ng = gsn - q0 < 0 ? 0 : (gsn - q0 < a.per ? gsn - q0 : a.per);
+    const int tb = (int)blockIdx.x * a.tpw;                  // < tiles by the grid
+    const int te = tb + a.tpw < a.tiles ? tb + a.tpw : a.tiles;
+    const XT *__restrict__ x = (const XT *)a.x;
 
-    const int64_t tb = (int64_t)blockIdx.x * tiles_per_wg;
-    int64_t te = tb + tiles_per_wg;
-    if (te > L.tiles) te = L.tiles;
-
-    // ---- code and scale words of the wave's groups, per tile ---------------
-    u4_t cw[GPW], cwn[GPW];
-    u2_t sw[GPW], swn[GPW];
-    auto load_tile = [&](int64_t t, u4_t (&c)[GPW], u2_t (&sc)[GPW]) {
-        const uint8_t *codes = packed + L.tile_codes(t) + (gs0 + q0) * kGroupCodeBytes + lane * 16;
-        const uint8_t *scales = packed + L.tile_scales(t) + (gs0 + q0) * kGroupScaleBytes + r * 8;
-#pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            if (q < ng) {
-                c[q] = load_u4(codes + q * kGroupCodeBytes);
-                sc[q] = load_u2(scales + q * kGroupScaleBytes);
-            }
-        }
-    };
-    // the first tile's words go out before x is staged: both latencies overlap
-    if (tb < te) load_tile(tb, cw, sw);
-
-    // ---- stage the slice of x as A fragments -------------------------------
-    // One pass over global memory: item = (block bl, row t, quarter gq) holds
-    // the 8 values k = 32bl + 4gq + {0..3} and 32bl + 16 + 4gq + {0..3}; each
-    // thread loads its items into registers, the workgroup reduces the per-row
-    // max |x| (through LDS), and the same registers are then scaled, split into
-    // high and low binary16 parts and written as fragments.
-    const int64_t k0 = gs0 * 128;                            // first k of the slice
-    const int kin = (int)((in - k0) < (int64_t)nbs * 32 ? (in - k0) : (int64_t)nbs * 32);
+    // ---- request the slice of x -------------------------------------------
+    // item = (block bl, row t, quarter gq): the 8 values k = 32bl + 4gq +
+    // {0..3} and 32bl + 16 + 4gq + {0..3}.
+    const int k0 = gs0 * 128;                                // first k of the slice
+    const int kin = a.in - k0 < nbs * 32 ? a.in - k0 : nbs * 32;
     const int items = nbs * NT * 4;
     float xv[kMaxItems][8];
-    float mloc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) mloc[t] = 0.0f;
 #pragma unroll
     for (int ii = 0; ii < kMaxItems; ++ii) {
         const int it = tid + ii * (int)blockDim.x;
@@ -146,11 +139,42 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) xv[ii][k] = 0.0f;
         if (it < items && bl * 32 < kin) {
-            const XT *p = x + (int64_t)t * in + k0 + 32 * bl + 4 * gq;
-            const float4 a = load_x4<XT>(p), c = load_x4<XT>(p + 16);
-            xv[ii][0] = a.x; xv[ii][1] = a.y; xv[ii][2] = a.z; xv[ii][3] = a.w;
-            xv[ii][4] = c.x; xv[ii][5] = c.y; xv[ii][6] = c.z; xv[ii][7] = c.w;
+            const XT *p = x + (int64_t)t * a.in + k0 + 32 * bl + 4 * gq;
+            const float4 u = load_x4<XT>(p), v = load_x4<XT>(p + 16);
+            xv[ii][0] = u.x; xv[ii][1] = u.y; xv[ii][2] = u.z; xv[ii][3] = u.w;
+            xv[ii][4] = v.x; xv[ii][5] = v.y; xv[ii][6] = v.z; xv[ii][7] = v.w;
         }
+    }
+
+    // ---- request the first tile's code and scale words --------------------
+    // Group q of the wave is slice group q0 + q; a wave with fewer than GPW
+    // groups (or none) repeats a valid address of its slice.
+    const int gw = ng > 0 ? gs0 + q0 : gs0;
+    const uint8_t *cbase = a.packed + a.code_base + (int64_t)gw * kGroupCodeBytes + lane * 16;
+    const uint8_t *sbase = a.packed + (int64_t)gw * kGroupScaleBytes + r * 8;
+    u4_t cw[GPW];
+    u2_t sw[GPW];
+    auto load_group = [&](int t, int q) {
+        const int64_t j = (int64_t)t * a.g4 + (q < ng ? q : 0);
+        cw[q] = load_u4(cbase + j * kGroupCodeBytes);
+        sw[q] = load_u2(sbase + j * kGroupScaleBytes);
+    };
+#pragma unroll
+    for (int q = 0; q < GPW; ++q) load_group(tb, q);
+    // keep the x reduction below the weight requests
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- stage the slice of x as A fragments -------------------------------
+    // The workgroup reduces each row's max |x| (through LDS), then each thread
+    // scales its items, splits them into high and low binary16 parts and
+    // writes them as fragments.
+    float mloc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mloc[t] = 0.0f;
+#pragma unroll
+    for (int ii = 0; ii < kMaxItems; ++ii) {
+        const int it = tid + ii * (int)blockDim.x;
+        const int t = (it >> 2) % NT;
         float m = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(xv[ii][k]));
@@ -208,74 +232,83 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(
     // row depends only on its own A row, and the rows of unused slots are
     // never read, so their contents do not matter (they stay finite).
     const int jslot = r < NT ? r : ((r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
-    const uint8_t *afrag = smem + (jslot * 4 + g) * 16;     // + bl * (2*NT*64)
-    constexpr int kFragStride = 2 * NT * 64;
+    constexpr int kFragStride = 2 * NT * 64;                 // bytes per block
+    const uint8_t *afrag = smem + (jslot * 4 + g) * 16 + q0 * 4 * kFragStride;
+    // D slots a lane can hold live: 4g+i for i < min(NT, 4)
+    constexpr int kLive = NT < 4 ? NT : 4;
     // inverse scale of the row behind D slot 4g+i (slot m and m+8 are one row)
-    float inv[4];
+    float inv[kLive];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLive; ++i) {
         const int row = (4 * g + i) & 7;
         float sc = 1.0f;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) sc = row == tt ? scale[tt] : sc;
         inv[i] = pow2f(127 - (int)(__builtin_bit_cast(uint32_t, sc) >> 23));
     }
+    const Magic mg = pinned_magic();
 
-    // ---- tiles --------------------------------------------------------------
+    // One tile: per group, four independent products (one per block), then
+    // acc += d * D on the live slots; the waves' sums meet in LDS.
     int par = 0;
-    for (int64_t t = tb; t < te; ++t) {
-        if (t + 1 < te) load_tile(t + 1, cwn, swn);
-        f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // With `next` set, group q's words of tile t + 1 are requested into the
+    // same registers as soon as group q of tile t has consumed them.
+    auto tile = [&](int t, bool next) {
+        float acc[kLive];
+#pragma unroll
+        for (int k = 0; k < kLive; ++k) acc[k] = 0.0f;
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (q < ng) {
-                const uint8_t *ag = afrag + (q0 + q) * 4 * kFragStride;
+                const uint8_t *ag = afrag + q * 4 * kFragStride;
+                f4_t dd[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const h8_t a = *reinterpret_cast<const h8_t *>(ag + s * kFragStride);
+                    const h8_t av = *reinterpret_cast<const h8_t *>(ag + s * kFragStride);
                     uint32_t qd[4];
-                    decode_word_pairs(cw[q][s], qd);
+                    decode_word_pairs(cw[q][s], mg, qd);
                     const f4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const f4_t dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pack_h8(qd), z, 0, 0, 0);
-                    const float d = (float)as_h2(sw[q][s >> 1])[s & 1];   // v_fma_mix operand
-                    // D slot 4g+k: with n <= 4 only k < n can be live (slots
-                    // 0..n-1 on g = 0 lanes, 8..8+n-1 on g = 2 lanes)
+                    dd[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pack_h8(qd), z, 0, 0, 0);
+                }
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (NT > 4 || k < NT) acc[k] = __builtin_fmaf(d, dd[k], acc[k]);
+                for (int s = 0; s < 4; ++s) {
+                    const float d = (float)as_h2(sw[q][s >> 1])[s & 1];   // v_fma_mix operand
+#pragma unroll
+                    for (int k = 0; k < kLive; ++k) acc[k] = __builtin_fmaf(d, dd[s][k], acc[k]);
                 }
             }
+            if (next) load_group(t + 1, q);
         }
         // undo the activation scale, add low parts (slots 8..15, lanes 32..63)
         // to high parts (slots 0..7, lanes 0..31)
-        float v[4];
+        float v[kLive];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kLive; ++i) {
             v[i] = acc[i] * inv[i];
             v[i] += __shfl_xor(v[i], 32);
         }
         if (g < 2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[par][wave][4 * g + i][r] = v[i];
+            for (int i = 0; i < kLive; ++i) red[par][wave][4 * g + i][r] = v[i];
         }
         __syncthreads();
         for (int e = tid; e < NT * 16; e += blockDim.x) {
             const int tt = e >> 4, rr = e & 15;
             float sum = 0.0f;
             for (int w = 0; w < nwaves; ++w) sum += red[par][w][tt][rr];
-            if (slices == 1) {
-                const int64_t row = t * kTileRows + rr;
-                if (row < out) y[(int64_t)tt * out + row] = sum;
+            if (gridDim.y == 1) {
+                const int row = t * kTileRows + rr;
+                if (row < a.out) a.y[(int64_t)tt * a.out + row] = sum;
             } else {
-                part[((sy * L.tiles + t) * 8 + tt) * 16 + rr] = sum;
+                a.part[(((int64_t)sy * a.tiles + t) * 8 + tt) * 16 + rr] = sum;
             }
         }
         par ^= 1;
-        if (t + 1 < te) {
-#pragma unroll
-            for (int q = 0; q < GPW; ++q) { cw[q] = cwn[q]; sw[q] = swn[q]; }
-        }
-    }
+    };
+
+    int t = tb;
+    for (; t + 1 < te; ++t) tile(t, true);
+    tile(t, false);
 }
 
 // y[t][row] = sum over the S slices of the parked per-tile sums, in slice order.
@@ -307,10 +340,21 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     if (gps_max < 1) gps_max = 1;
     p.slices = (L.g4 + gps_max - 1) / gps_max;
     p.gps = (L.g4 + p.slices - 1) / p.slices;
-    // waves: 4, or 8 for long slices; groups per wave within the template bound
-    p.waves = p.gps > 20 ? 8 : 4;
-    int per = (int)((p.gps + p.waves - 1) / p.waves);
-    p.gpw = per <= 2 ? 2 : per <= 5 ? 5 : per <= 8 ? 8 : per <= 12 ? 12 : 16;
+    // about five groups per wave (5.6 KB of words in flight per wave per
+    // tile), at most eight waves; the register capacity rounds up to a
+    // compiled size
+    int64_t waves = (p.gps + 4) / 5;
+    // enough threads to hold the slice of x while it is staged
+    const int64_t items = p.gps * 4 * n * 4;
+    const int64_t stage_waves = (items + kMaxItems * 64 - 1) / (kMaxItems * 64);
+    if (waves < stage_waves) waves = stage_waves;
+    if (waves > kMfmaMaxWaves) waves = kMfmaMaxWaves;
+    if (waves < 1) waves = 1;
+    p.per = (int)((p.gps + waves - 1) / waves);
+    p.waves = (int)((p.gps + p.per - 1) / p.per);
+    p.gpw = 0;
+    for (int v : kGpwSet)
+        if (p.gpw == 0 && v >= p.per) p.gpw = v;
     // about kMfmaTargetWgs workgroups in all, each walking a run of tiles
     int64_t tpw = (L.tiles * p.slices + kMfmaTargetWgs - 1) / kMfmaTargetWgs;
     if (tpw < 1) tpw = 1;
@@ -330,8 +374,9 @@ bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     (void)x_f16;
     if (n < 1 || n > 8) return false;
     const MfmaPlan p = mfma_plan(n, out, in);
-    if (p.waves > kMfmaMaxWaves || p.slices > 65535 || p.gx > 0x7fffffff) return false;
-    if ((int64_t)p.waves * p.gpw < p.gps) return false;
+    if (p.gpw == 0 || p.waves > kMfmaMaxWaves || p.slices > 65535 || p.gx > 0x7fffffff)
+        return false;
+    if ((int64_t)p.waves * p.per < p.gps) return false;
     if (p.gps * 4 * n * 4 > (int64_t)kMaxItems * p.waves * 64) return false;
     return gemv_mfma_workspace_bytes(n, out, in) <= kWorkspaceBytes;
 }
@@ -341,23 +386,35 @@ static hipError_t launch_mfma_t(const void *packed, const void *x, float *y, int
                                 int64_t in, void *ws, hipStream_t stream) {
     const MfmaPlan p = mfma_plan(NT, out, in);
     const Layout L(out, in);
-    float *part = p.slices > 1 ? (float *)ws : nullptr;
+    MfmaArgs a;
+    a.packed = (const uint8_t *)packed;
+    a.x = x;
+    a.y = y;
+    a.part = p.slices > 1 ? (float *)ws : nullptr;
+    a.code_base = L.scale_bytes();
+    a.out = (int)out;
+    a.in = (int)in;
+    a.g4 = (int)L.g4;
+    a.tiles = (int)L.tiles;
+    a.gps = (int)p.gps;
+    a.per = p.per;
+    a.tpw = (int)p.tpw;
     const dim3 gd((unsigned)p.gx, (unsigned)p.slices), bd(p.waves * 64);
     const size_t lds = (size_t)mfma_lds_bytes(NT, p.gps);
-    const uint8_t *pk = (const uint8_t *)packed;
-    const XT *xx = (const XT *)x;
     switch (p.gpw) {
-    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 2>), gd, bd, lds, stream, pk, xx, y, out, in, p.gps, p.tpw, part); break;
-    case 5: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 5>), gd, bd, lds, stream, pk, xx, y, out, in, p.gps, p.tpw, part); break;
-    case 8: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 8>), gd, bd, lds, stream, pk, xx, y, out, in, p.gps, p.tpw, part); break;
-    case 12: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 12>), gd, bd, lds, stream, pk, xx, y, out, in, p.gps, p.tpw, part); break;
-    default: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 16>), gd, bd, lds, stream, pk, xx, y, out, in, p.gps, p.tpw, part); break;
+    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 2>), gd, bd, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 4>), gd, bd, lds, stream, a); break;
+    case 5: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 5>), gd, bd, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 8>), gd, bd, lds, stream, a); break;
+    case 10: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 10>), gd, bd, lds, stream, a); break;
+    case 16: hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, 16>), gd, bd, lds, stream, a); break;
+    default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.slices == 1) return e;
     const int64_t total = L.tiles * NT * 16;
     hipLaunchKernelGGL((gemv_mfma_reduce_kernel<NT>), dim3((unsigned)grid_for(total, 256)),
-                       dim3(256), 0, stream, (const float *)part, y, out, L.tiles, p.slices);
+                       dim3(256), 0, stream, (const float *)a.part, y, out, L.tiles, p.slices);
     return hipGetLastError();
 }
 
