@@ -148,7 +148,14 @@ int q4_0_matmul_ex(const void *packed, const void *x, int x_dtype, float *y, int
         }
         return map_hip(q4::launch_gemv_mfma(packed, x, x_f16, y, n, out, in, ws, s));
     }
-    default: return map_hip(q4::launch_gemm(packed, x, x_f16, y, n, out, in, s));
+    default: {
+        void *ws = nullptr;
+        if (q4::gemm_workspace_bytes(n, out, in) > 0) {
+            const int wst = get_workspace(s, &ws);
+            if (wst != Q4_0_OK) return wst;
+        }
+        return map_hip(q4::launch_gemm(packed, x, x_f16, y, n, out, in, ws, s));
+    }
     }
 }
 

@@ -4,210 +4,570 @@
 // is prefill's workhorse; golem reads prompts in passes of up to 512
 // positions, golem README "Reading a prompt on the card").
 //
-// Tile: a workgroup of four waves computes 64 activation rows x 256 weight
-// rows; wave w owns weight rows [64w, 64w+64) of the tile (four 16-row tiles)
-// against all 64 activation rows, as 4 x 4 accumulators of
-// v_mfma_f32_16x16x32_f16 (one MFMA K step = one Q4_0 block).
+// Instruction: v_mfma_f32_32x32x16_f16.  On gfx950 it retires twice the
+// flops per cycle of v_mfma_f32_16x16x32_f16, and each issue leaves about
+// four VALU slots free; the weight decode costs 14 VALU operations per 8
+// weights, so every decoded B fragment is reused by four MFMAs.
 //
-// Operands per K step of four blocks (128 k):
-//   x: 64 rows x 128 k of binary16, staged in LDS (double buffered) in MFMA
-//      A-fragment order: for each row and block, the eight k-values a lane
-//      with quarter g needs (4g..4g+3 and 4g+16..4g+19) are 16 contiguous
-//      bytes, read with one ds_read_b128.  float32 activations are rounded to
-//      binary16 when staged.
-//   W: each lane loads its own 16-byte code word and 8-byte scale word per
-//      16-row tile straight from the repacked stream (the word is the MFMA
-//      B fragment), decodes exact q - 8 and multiplies by d in binary16, so
-//      each weight is rounded once.  The next step's words are loaded before
-//      the current step is computed.
+// Tile: a workgroup of four waves computes 128 activation rows x 128 weight
+// rows.  Wave (wn, wk) owns weight rows [64 wn, 64 wn + 64) of the tile and
+// blocks 2 wk, 2 wk + 1 of every 4-block group (128 k) of the workgroup's K
+// slice: 4 x 2 accumulators of 32 x 32 against all 128 activation rows, so
+// each A fragment read from LDS feeds two MFMAs.  At the end the two K halves
+// are summed through LDS.
+//
+// Operands of one MFMA (K = 16, half a Q4_0 block):
+//   A: lane l = 32h + m holds activation row m of its 32-row sub-tile at
+//      k = 16ks + 8h .. +7 of the group (natural order, 16 bytes).  The
+//      group's x tile (128 rows x 128 k, binary16) is staged in LDS, four
+//      groups ahead (direct copies from global memory for binary16 x;
+//      float32 x goes through registers and is rounded to binary16).
+//   B: lane l = 32h + c holds weight row c of a 32-row sub-tile at the same
+//      k.  k = 8h..8h+7 of a block are the low nibbles of code bytes
+//      8h..8h+7, k = 16+8h.. their high nibbles, so the lane loads the
+//      repacked words of quarters 2h and 2h+1 (4 bytes per block) and one
+//      word pair yields the B fragments of both K halves of a block.  Each
+//      value is exact q - 8 times d, rounded once to binary16.
+//   D: lane l holds weight row l%32 and activation rows 8(i/4) + 4h + i%4.
+//
+// Work split: workgroups are (M block, N block, K slice).  When the tiles
+// alone cannot fill the device the K range is cut into S slices whose
+// partial sums go to a workspace; a second kernel adds them in slice order.
+// Consecutive workgroup ids are dealt to the eight dies in turn; the ids are
+// permuted so that each die takes a contiguous run of tiles in which the M
+// blocks of one N block are adjacent, and its L2 serves their shared words.
+#include <type_traits>
+
 #include "q4_0_device.h"
 #include "q4_0_internal.h"
 
 namespace q4 {
 
-constexpr int kGemmBM = 64;                  // activation rows per workgroup
-constexpr int kGemmBN = 256;                 // weight rows per workgroup
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmBM = 128;                 // activation rows per workgroup
+constexpr int kGemmBN = 128;                 // weight rows per workgroup
 constexpr int kGemmWaves = 4;
-constexpr int kGemmTilesPerWave = kGemmBN / kGemmWaves / kTileRows;  // 4
-constexpr int kGemmMSub = kGemmBM / 16;      // 4
-constexpr int kXRowBytes = 4 * 4 * 16 + 16;  // one row of a K step, padded
+constexpr int kGemmMSub = kGemmBM / 32;      // 32-row sub-tiles per wave
+constexpr int kStepBytes = kGemmBM * 128 * 2;  // one step's x tile: 32 KB
+constexpr int kPiecesPerThread = kStepBytes / 16 / (kGemmWaves * 64);  // 8
+constexpr int kXBytes = kStepBytes;              // x part of a stage
+constexpr int kWBytes = 8 * kGroupCodeBytes;      // code words of the 8 repacked tiles
+constexpr int kSBytes = 4 * 1024;                 // their scales: a 1 KB slot per wave
+constexpr int kStageBytes = kXBytes + kWBytes + kSBytes;   // 44 KB
+constexpr int kStages = 3;                        // LDS ring: 132 KB
+constexpr int kCopies = kPiecesPerThread + 3;     // copies per wave per step (binary16 x)
+constexpr int kCopyParts012 = 9;                  // copies in parts 0..2 of a step
+constexpr int kTileStride = 136;                  // epilogue tile row, floats
+constexpr int kEpiBytes = kGemmBM * kTileStride * 4;   // 68 KB
+constexpr int kGemmLds = kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
+static_assert(kGemmLds <= 160 * 1024, "LDS of one workgroup");
+constexpr int kDies = 8;
+constexpr int kComputeUnits = 256;
 
-template <typename XT>
-__device__ __forceinline__ void load_x_piece(const XT *__restrict__ src, bool ok, uint32_t h[4]);
+struct GemmArgs {
+    const uint8_t *packed;
+    const void *x;
+    float *y;
+    float *part;          // S partial products, S x n x out, when S > 1
+    int64_t code_base;    // byte offset of the code stream
+    int n, out, in;
+    int g4, tiles;        // layout: groups per row, 16-row tiles
+    int nm, nn, slices;   // M blocks, N blocks, K slices
+    int gps;              // groups per K slice
+    int die_map;          // permute ids per die
+};
 
-// 8 consecutive binary16 values
-template <>
-__device__ __forceinline__ void load_x_piece<_Float16>(const _Float16 *__restrict__ src, bool ok,
-                                                       uint32_t h[4]) {
+// 8 consecutive float32 activations (zeros when !ok), and their binary16 form
+struct X8 {
+    float4 a, b;
+};
+__device__ __forceinline__ X8 load_x8(const float *__restrict__ src, bool ok) {
+    X8 v = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (ok) {
-        const u4_t v = *reinterpret_cast<const u4_t *>(src);
-        h[0] = v[0]; h[1] = v[1]; h[2] = v[2]; h[3] = v[3];
-    } else {
-        h[0] = h[1] = h[2] = h[3] = 0u;
+        v.a = *reinterpret_cast<const float4 *>(src);
+        v.b = *reinterpret_cast<const float4 *>(src + 4);
     }
+    return v;
+}
+__device__ __forceinline__ u4_t to_half8(const X8 &v) {
+    u4_t h;
+    h[0] = as_u32(h2_t{(_Float16)v.a.x, (_Float16)v.a.y});
+    h[1] = as_u32(h2_t{(_Float16)v.a.z, (_Float16)v.a.w});
+    h[2] = as_u32(h2_t{(_Float16)v.b.x, (_Float16)v.b.y});
+    h[3] = as_u32(h2_t{(_Float16)v.b.z, (_Float16)v.b.w});
+    return h;
 }
 
-// 8 consecutive float32 values rounded to binary16
-template <>
-__device__ __forceinline__ void load_x_piece<float>(const float *__restrict__ src, bool ok,
-                                                    uint32_t h[4]) {
-    if (ok) {
-        const float4 a = *reinterpret_cast<const float4 *>(src);
-        const float4 b = *reinterpret_cast<const float4 *>(src + 4);
-        h[0] = as_u32(h2_t{(_Float16)a.x, (_Float16)a.y});
-        h[1] = as_u32(h2_t{(_Float16)a.z, (_Float16)a.w});
-        h[2] = as_u32(h2_t{(_Float16)b.x, (_Float16)b.y});
-        h[3] = as_u32(h2_t{(_Float16)b.z, (_Float16)b.w});
-    } else {
-        h[0] = h[1] = h[2] = h[3] = 0u;
-    }
+// Direct copy of 16 bytes per lane from global memory into LDS (no register
+// round trip): the wave's 64 lanes fill 1 KB at `lds` (wave-uniform), lane i
+// at lds + 16 i.  Written as inline assembly on purpose: the compiler does not
+// know which LDS bytes such a copy writes, so for its own copy instruction it
+// waits for every outstanding copy before each later LDS read, which would
+// drain the multi-stage pipeline below.  Here the copies are invisible to it
+// and the kernel waits for them explicitly (vector-memory count, then a
+// barrier) before reading a stage.  M0 holds the LDS base; one wait state
+// separates its write from the copy.
+__device__ __forceinline__ void dma16(const void *src, uint8_t *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(base)
+                 : "memory", "m0");
 }
 
+__device__ const u4_t kZeroPiece = {0u, 0u, 0u, 0u};
+
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt left
+// free): vmcnt is bits 3:0 and 15:14 of the immediate.
+#define Q4_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+#define Q4_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+
 template <typename XT>
-__global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
-    const uint8_t *__restrict__ packed, const XT *__restrict__ x, float *__restrict__ y,
-    int64_t n, int64_t out, int64_t in) {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kGemmBM * kXRowBytes];
-    const Layout L(out, in);
+__global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // kGemmLds bytes
+    constexpr bool kDma = sizeof(XT) == 2;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, c = lane & 31;
     const Magic mg = pinned_magic();
-    const int g = lane >> 4, r = lane & 15;
-    const int64_t m0 = (int64_t)blockIdx.y * kGemmBM;
-    const int64_t tile0 = (int64_t)blockIdx.x * (kGemmBN / kTileRows) + wave * kGemmTilesPerWave;
-    const int64_t nsteps = L.g4;
 
-    // ---- staging of x: 64 rows x 16 pieces of 8 values per step -----------
-    // piece p of a row covers k = 8p..8p+7 of the step: block s = p/4, offset
-    // o = 8*(p%4) in the block.  Its first 4 values go to quarter
-    // g = 2*((p%4)&1) (o = 0 or 16 -> g 0; o = 8 or 24 -> g 2) and the next
-    // 4 to g + 1; o < 16 fills the first half of the 16-byte fragment,
-    // o >= 16 the second half.
-    uint32_t xh[4][4];
-    auto load_x_step = [&](int64_t step) {
+    // ---- which tile and K slice -------------------------------------------
+    int id = blockIdx.x;
+    const int total = a.nm * a.nn * a.slices;
+    if (a.die_map) id = (id % kDies) * (total / kDies) + id / kDies;
+    const int mb = id % a.nm;
+    const int rest = id / a.nm;
+    const int nb = rest % a.nn;
+    const int sl = rest / a.nn;
+    const int wn = wave & 1, wk = wave >> 1;
+    const int m0 = mb * kGemmBM;
+    const int gs0 = sl * a.gps;
+    const int gs1 = gs0 + a.gps < a.g4 ? gs0 + a.gps : a.g4;
+    const int nsteps = gs1 - gs0;
+    const XT *__restrict__ x = (const XT *)a.x;
+
+    // ---- copies of one step into a stage -----------------------------------
+    // x: 128 activation rows x 16 chunks of 8 binary16 (chunk q = k 8q..8q+7
+    // of the group), row-major, the chunks of row r XOR-swizzled: chunk q of
+    // row r sits in slot r * 16 + (q ^ (r & 15)).  A copy instruction fills 64
+    // consecutive slots = 4 whole rows (coalesced reads); the fragment reads
+    // hit 16 distinct slot columns per 16 lanes (no bank conflict).  Wave w
+    // fills rows 32 w .. 32 w + 31, copy i rows 32 w + 4 i + lane / 16.  Rows
+    // past n repeat row n - 1 (a D row depends only on its own A row, and
+    // those rows are not stored); in a group that runs past in, k >= in is
+    // zero.
+    // W: the group's code words of the tile's 8 repacked 16-row tiles (1 KB
+    // each, as stored) and their scales; wave w copies tiles 2w, 2w + 1 and
+    // their scales (lanes 0..15 carry the 256 scale bytes, the other lanes
+    // repeat them into the rest of the wave's 1 KB scale slot, so the copy
+    // needs no branch).  Tiles past the matrix read the last tile (their
+    // scales are forced to zero when used).
+    uint32_t xoff[kPiecesPerThread];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + q * 256;
-            const int row = c >> 4, p = c & 15;
-            const int64_t tok = m0 + row;
-            const int64_t k = step * 128 + 8 * p;
-            const bool ok = tok < n && k < in;
-            load_x_piece<XT>(x + tok * in + k, ok, xh[q]);
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+        const int r = 32 * wave + 4 * i + (lane >> 4);
+        const int q = (lane & 15) ^ (r & 15);
+        const int rr = m0 + r < a.n ? r : a.n - 1 - m0;
+        xoff[i] = ((uint32_t)rr * a.in + 8 * q) * (uint32_t)sizeof(XT);
+    }
+    const XT *xbase = x + (int64_t)m0 * a.in;
+    const int t0 = nb * (kGemmBN / kTileRows);               // first repacked tile
+    int tw[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = t0 + 2 * wave + u;
+        tw[u] = t < a.tiles ? t : a.tiles - 1;
+    }
+    const int ts = tw[(lane >> 3) & 1];
+    const uint32_t soff_copy = (uint32_t)ts * a.g4 * kGroupScaleBytes + (lane & 7) * 16;
+
+    // part p of step st's copies: x pieces 3p .. 3p+2 (binary16 x only),
+    // code tile 2w at p = 2, code tile 2w + 1 and the scales at p = 3
+    auto fill = [&](int st, int part, bool partial) {
+        const int j = gs0 + st;
+        uint8_t *stage = lds + (st % kStages) * kStageBytes;
+        if constexpr (kDma) {
+            uint8_t *xd = stage + wave * 8192;
+            const uint8_t *src = (const uint8_t *)(xbase + j * 128);
+#pragma unroll
+            for (int i = 0; i < kPiecesPerThread; ++i) {
+                if (i < 3 * part || i >= (part < 2 ? 3 * part + 3 : kPiecesPerThread)) continue;
+                const void *p = src + xoff[i];
+                if (partial) {
+                    const int r = 32 * wave + 4 * i + (lane >> 4);
+                    const int q = (lane & 15) ^ (r & 15);
+                    p = j * 128 + 8 * q < a.in ? p : (const void *)&kZeroPiece;
+                }
+                dma16(p, xd + i * 1024);
+            }
+        }
+        if (part == 2)
+            dma16(a.packed + a.code_base + ((int64_t)tw[0] * a.g4 + j) * kGroupCodeBytes + lane * 16,
+                  stage + kXBytes + (2 * wave) * 1024);
+        if (part == 3) {
+            dma16(a.packed + a.code_base + ((int64_t)tw[1] * a.g4 + j) * kGroupCodeBytes + lane * 16,
+                  stage + kXBytes + (2 * wave + 1) * 1024);
+            dma16(a.packed + (int64_t)j * kGroupScaleBytes + soff_copy,
+                  stage + kXBytes + kWBytes + wave * 1024);
         }
     };
-    auto store_x_step = [&](int buf) {
+    X8 xp[kDma ? 1 : kPiecesPerThread];
+    auto fetch = [&](int st) {                     // register path (float32 x): load
+        if constexpr (!kDma) {
+            const int j = gs0 + st;
+            const uint8_t *src = (const uint8_t *)(xbase + j * 128);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + q * 256;
-            const int row = c >> 4, p = c & 15;
-            const int s = p >> 2, pq = p & 3;
-            const int ga = (pq & 1) * 2, half = pq >> 1;
-            uint8_t *base = xs[buf] + row * kXRowBytes + s * 64 + half * 8;
-            *reinterpret_cast<u2_t *>(base + ga * 16) = u2_t{xh[q][0], xh[q][1]};
-            *reinterpret_cast<u2_t *>(base + (ga + 1) * 16) = u2_t{xh[q][2], xh[q][3]};
-        }
-    };
-
-    // ---- weight words: 4 tiles x (16-byte codes + 8-byte scales) per step --
-    u4_t cw[kGemmTilesPerWave], cwn[kGemmTilesPerWave];
-    u2_t sw[kGemmTilesPerWave], swn[kGemmTilesPerWave];
-    auto load_w_step = [&](int64_t step, u4_t (&c)[kGemmTilesPerWave],
-                           u2_t (&sc)[kGemmTilesPerWave]) {
-#pragma unroll
-        for (int ni = 0; ni < kGemmTilesPerWave; ++ni) {
-            const int64_t t = tile0 + ni;
-            if (t < L.tiles) {
-                c[ni] = load_u4(packed + L.tile_codes(t) + step * kGroupCodeBytes + lane * 16);
-                sc[ni] = load_u2(packed + L.tile_scales(t) + step * kGroupScaleBytes + r * 8);
-            } else {
-                c[ni] = u4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-                sc[ni] = u2_t{0u, 0u};
+            for (int i = 0; i < kPiecesPerThread; ++i) {
+                const int r = 32 * wave + 4 * i + (lane >> 4);
+                const int q = (lane & 15) ^ (r & 15);
+                const bool ok = j * 128 + 8 * q < a.in;
+                xp[i] = load_x8((const float *)(src + xoff[i]), ok);
             }
         }
     };
-
-    f4_t acc[kGemmMSub][kGemmTilesPerWave];
+    auto park = [&](int st) {                      // register path: convert, write the stage
+        if constexpr (!kDma) {
+            uint8_t *xd = lds + (st % kStages) * kStageBytes + wave * 8192 + lane * 16;
 #pragma unroll
-    for (int mi = 0; mi < kGemmMSub; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kGemmTilesPerWave; ++ni) acc[mi][ni] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-    load_x_step(0);
-    load_w_step(0, cw, sw);
-    store_x_step(0);
-    __syncthreads();
-
-    int buf = 0;
-    for (int64_t step = 0; step < nsteps; ++step) {
-        const bool more = step + 1 < nsteps;
-        if (more) {
-            load_x_step(step + 1);
-            load_w_step(step + 1, cwn, swn);
+            for (int i = 0; i < kPiecesPerThread; ++i)
+                *reinterpret_cast<u4_t *>(xd + i * 1024) = to_half8(xp[i]);
         }
+    };
+    // fragment read offsets: lane (h, m) reads row 32 mi + m, chunk 2 ks + h
+    uint32_t aoff[8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            h8_t a[kGemmMSub];
+    for (int ks = 0; ks < 8; ++ks) aoff[ks] = c * 256 + 16 * ((2 * ks + h) ^ (c & 15));
+    // weight words of the lane in a stage: sub-tile ni = rows 64 wn + 32 ni + c
+    // = tile 4 wn + 2 ni + c / 16, row c % 16; quarter 2h (+1: 256 bytes on),
+    // blocks 2 wk, 2 wk + 1 (8 bytes); their scales (4 bytes) in the slot of
+    // the wave that copied the tile
+    uint32_t woff[2], sgoff[2];
+    bool wvalid[2];
 #pragma unroll
-            for (int mi = 0; mi < kGemmMSub; ++mi) {
-                const uint8_t *p = xs[buf] + (mi * 16 + r) * kXRowBytes + s * 64 + g * 16;
-                a[mi] = __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t *>(p));
-            }
-#pragma unroll
-            for (int ni = 0; ni < kGemmTilesPerWave; ++ni) {
-                uint32_t q[4];
-                decode_word(cw[ni][s], mg, q);
-                const uint32_t dbits = (sw[ni][s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
-                const h2_t d2 = as_h2(dbits | (dbits << 16));
-#pragma unroll
-                for (int k = 0; k < 4; ++k) q[k] = as_u32(as_h2(q[k]) * d2);
-                const h8_t bfrag = pack_h8(q);
-#pragma unroll
-                for (int mi = 0; mi < kGemmMSub; ++mi)
-                    acc[mi][ni] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], bfrag, acc[mi][ni], 0, 0, 0);
-            }
-        }
-        if (more) {
-            store_x_step(buf ^ 1);
-#pragma unroll
-            for (int ni = 0; ni < kGemmTilesPerWave; ++ni) { cw[ni] = cwn[ni]; sw[ni] = swn[ni]; }
-        }
-        __syncthreads();
-        buf ^= 1;
+    for (int ni = 0; ni < 2; ++ni) {
+        const int tl = 4 * wn + 2 * ni + (c >> 4);
+        wvalid[ni] = t0 + tl < a.tiles;
+        woff[ni] = kXBytes + tl * 1024 + ((2 * h) * 16 + (c & 15)) * 16 + 8 * wk;
+        sgoff[ni] = kXBytes + kWBytes + (tl >> 1) * 1024 + (tl & 1) * 128 + (c & 15) * 8 + 4 * wk;
     }
 
-    // ---- epilogue: D slot 4g+i of M sub-tile mi, weight row r of tile ni ---
+    f16x_t acc[kGemmMSub][2];
 #pragma unroll
     for (int mi = 0; mi < kGemmMSub; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < kGemmTilesPerWave; ++ni) {
-            const int64_t row = (tile0 + ni) * kTileRows + r;
-            if (row >= out) continue;
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t tok = m0 + mi * 16 + 4 * g + i;
-                if (tok < n) y[tok * out + row] = acc[mi][ni][i];
+            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+    const h2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+
+    // ---- operands ------------------------------------------------------------
+    // The wave's part of a group: blocks 2wk, 2wk+1 = K-steps ks = 4wk+kq,
+    // kq = 0..3.  K-step kq uses A from the stage and, per sub-tile, B = low
+    // (kq even) or high (kq odd) nibbles of block 2wk + kq / 2.
+    u2_t w0[2], w1[2];                                       // code words of the step
+    uint32_t sc[2];                                          // their scales
+    uint32_t p01a[2], p23a[2], p01b[2], p23b[2];            // byte-spread words of a block
+    h2_t d2[2];
+    h8_t A[2][kGemmMSub];
+    h8_t B[2][2];
+    auto read_w = [&](int st) {
+        const uint8_t *stage = lds + (st % kStages) * kStageBytes;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            w0[ni] = *reinterpret_cast<const u2_t *>(stage + woff[ni]);
+            w1[ni] = *reinterpret_cast<const u2_t *>(stage + woff[ni] + 256);
+            sc[ni] = *reinterpret_cast<const uint32_t *>(stage + sgoff[ni]);
+        }
+    };
+    auto spread = [&](int b) {                              // b: 0 or 1, block 2wk + b
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            const uint32_t u0 = w0[ni][b], u1 = w1[ni][b];
+            p01a[ni] = __builtin_amdgcn_perm(u0, u0, 0x0C010C00u);
+            p23a[ni] = __builtin_amdgcn_perm(u0, u0, 0x0C030C02u);
+            p01b[ni] = __builtin_amdgcn_perm(u1, u1, 0x0C010C00u);
+            p23b[ni] = __builtin_amdgcn_perm(u1, u1, 0x0C030C02u);
+            const _Float16 d = wvalid[ni] ? as_h2(sc[ni])[b] : (_Float16)0.0f;
+            d2[ni] = h2_t{d, d};
+        }
+    };
+    auto frag = [&](bool hi, int ni) -> h8_t {
+        const uint32_t mask = hi ? kMaskHi : kMaskLo;
+        const uint32_t magic = hi ? mg.hi : mg.lo;
+        const h2_t off = hi ? off_hi : off_lo;
+        u4_t b;
+        b[0] = as_u32((as_h2((p01a[ni] & mask) | magic) + off) * d2[ni]);
+        b[1] = as_u32((as_h2((p23a[ni] & mask) | magic) + off) * d2[ni]);
+        b[2] = as_u32((as_h2((p01b[ni] & mask) | magic) + off) * d2[ni]);
+        b[3] = as_u32((as_h2((p23b[ni] & mask) | magic) + off) * d2[ni]);
+        return __builtin_bit_cast(h8_t, b);
+    };
+    auto read_a = [&](int st, int kq, h8_t (&av)[kGemmMSub]) {
+        const uint8_t *stage = lds + (st % kStages) * kStageBytes;
+#pragma unroll
+        for (int mi = 0; mi < kGemmMSub; ++mi)
+            av[mi] = __builtin_bit_cast(
+                h8_t, *reinterpret_cast<const u4_t *>(stage + aoff[4 * wk + kq] + mi * 8192));
+    };
+    // operands of K-step 0 of step st into buffer 0
+    auto prep_first = [&](int st) {
+        read_w(st);
+        read_a(st, 0, A[0]);
+        spread(0);
+        B[0][0] = frag(false, 0);
+        B[0][1] = frag(false, 1);
+    };
+    // Interleave: one MFMA, then an LDS read and up to four VALU operations.
+    // A wave issues in order and each MFMA holds the issue port while the
+    // matrix pipe takes it, so only work placed between the products
+    // overlaps them; the scheduling groups enforce that order inside the
+    // (branch-free) region.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2 * kGemmMSub; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto products = [&](int cur) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int mi = 0; mi < kGemmMSub; ++mi)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][mi], B[cur][ni],
+                                                                     acc[mi][ni], 0, 0, 0);
+    };
+
+    // ---- one step --------------------------------------------------------------
+    // K-steps 0..2 multiply while preparing K-step kq + 1 and issuing copy
+    // parts 0..2 of step st + 2.  Then a wait until step st + 1's copies have
+    // landed (its last part was issued one step ago; only parts 0..2 of step
+    // st + 2 are newer) and a barrier.  K-step 3 multiplies while issuing
+    // part 3 of step st + 2 and preparing K-step 0 of step st + 1.  The
+    // barrier also frees stage st for the copies of step st + 3.
+    // REQ: step st + 2 exists; PART: its group runs past in; NEXT: st + 1
+    // exists.
+    auto step = [&](int st, auto req_t, auto part_t, auto next_t) {
+        constexpr bool REQ = decltype(req_t)::value;
+        constexpr bool PART = decltype(part_t)::value;
+        constexpr bool NEXT = decltype(next_t)::value;
+        if constexpr (REQ && !kDma) fetch(st + kStages - 1);
+#pragma unroll
+        for (int kq = 0; kq < 3; ++kq) {
+            const int cur = kq & 1;
+            products(cur);
+            read_a(st, kq + 1, A[cur ^ 1]);
+            if (kq == 1) spread(1);
+            B[cur ^ 1][0] = frag(kq != 1, 0);
+            B[cur ^ 1][1] = frag(kq != 1, 1);
+            if (REQ) fill(st + kStages - 1, kq, PART);
+            interleave();
+        }
+        if constexpr (NEXT) {
+            if constexpr (REQ) Q4_WAIT_VMCNT(kCopyParts012);
+            else Q4_WAIT_VMCNT(0);
+            Q4_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();
+        }
+        products(1);
+        if (REQ) fill(st + kStages - 1, 3, PART);
+        if constexpr (NEXT) prep_first(st + 1);
+        interleave();
+        if constexpr (REQ && !kDma) park(st + kStages - 1);
+    };
+
+    // ---- pipeline ------------------------------------------------------------
+    // Steps 0 and 1 are requested up front, step st + 2 during step st; all
+    // requests are direct copies into LDS whose counts are managed here (the
+    // loop holds no loads into registers, so the compiler adds no waits).
+    // The float32 path stages x through registers instead: loaded at the top
+    // of step st, converted and written at its end.
+    for (int p = 0; p < kStages - 1 && p < nsteps; ++p) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) fill(p, part, (gs0 + p) * 128 + 128 > a.in);
+        if constexpr (!kDma) { fetch(p); park(p); }
+    }
+    if (nsteps > 1) Q4_WAIT_VMCNT(kCopies);
+    else Q4_WAIT_VMCNT(0);
+    Q4_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    prep_first(0);
+    // The steady state runs one variant of the step (the next-but-one step
+    // exists and its group lies inside the row); the at most three last
+    // steps are peeled, so the accumulators keep one register assignment
+    // through the loop.
+    using T = std::true_type;
+    using F = std::false_type;
+    const bool last_partial = gs1 * 128 > a.in;              // the slice's last group runs past in
+    const int n_main = nsteps - (kStages - 1) - (last_partial ? 1 : 0);
+    int st = 0;
+    for (; st < n_main; ++st) step(st, T(), F(), T());
+    if (last_partial && st == nsteps - kStages) step(st++, T(), T(), T());
+    if (st == nsteps - 2) step(st++, F(), F(), T());
+    if (st == nsteps - 1) step(st++, F(), F(), F());
+    Q4_WAIT_VMCNT(0);
+    Q4_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+
+    // ---- epilogue ------------------------------------------------------------
+    // The K half wk = 1 writes its sums into a row-major tile in LDS (row
+    // stride 136 floats: the two row groups of a write instruction land in
+    // disjoint banks); wk = 0 reads them all, adds its own and writes the
+    // tile back; then all four waves store whole rows, 16 bytes per lane.
+    // Reads before writes: the compiler keeps LDS accesses that may alias in
+    // program order, so interleaving them would serialize on LDS latency.
+    float *tile = reinterpret_cast<float *>(lds);            // 128 x 136 floats
+    // lane holds tile column 64 wn + 32 ni + c, tile rows
+    // 32 mi + 8 (v / 4) + 4 h + v % 4
+    auto tix = [&](int mi, int ni, int v) {
+        return (32 * mi + 8 * (v >> 2) + 4 * h + (v & 3)) * kTileStride + 64 * wn + 32 * ni + c;
+    };
+    if (wk == 1) {
+#pragma unroll
+        for (int mi = 0; mi < kGemmMSub; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) tile[tix(mi, ni, v)] = acc[mi][ni][v];
+    }
+    Q4_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    if (wk == 0) {
+        float other[kGemmMSub][2][16];
+#pragma unroll
+        for (int mi = 0; mi < kGemmMSub; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) other[mi][ni][v] = tile[tix(mi, ni, v)];
+#pragma unroll
+        for (int mi = 0; mi < kGemmMSub; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) tile[tix(mi, ni, v)] = acc[mi][ni][v] + other[mi][ni][v];
+    }
+    Q4_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    float *dst = a.slices > 1 ? a.part + (int64_t)sl * a.n * a.out : a.y;
+    const int n0 = nb * kGemmBN;
+    const bool full_cols = n0 + kGemmBN <= a.out && (a.out & 3) == 0;
+#pragma unroll 4
+    for (int it = 0; it < kGemmBM * kGemmBN / 4 / (kGemmWaves * 64); ++it) {
+        const int e = it * kGemmWaves * 64 + tid;              // float4 index in the tile
+        const int row = e >> 5, col = (e & 31) * 4;
+        if (m0 + row >= a.n) continue;
+        const float4 v = *reinterpret_cast<const float4 *>(tile + row * kTileStride + col);
+        float *yp = dst + (int64_t)(m0 + row) * a.out + n0 + col;
+        if (full_cols) {
+            *reinterpret_cast<float4 *>(yp) = v;
+        } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (n0 + col + q < a.out) yp[q] = vv[q];
+        }
+    }
+}
+
+// y = sum over the S slices of the partial products, in slice order.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ part,
+                                                          float *__restrict__ y, int64_t count,
+                                                          int slices) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; e < count; e += stride) {
+        if (e + 4 <= count) {
+            float4 s = *reinterpret_cast<const float4 *>(part + e);
+            for (int q = 1; q < slices; ++q) {
+                const float4 t = *reinterpret_cast<const float4 *>(part + (int64_t)q * count + e);
+                s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+            }
+            *reinterpret_cast<float4 *>(y + e) = s;
+        } else {
+            for (int64_t f = e; f < count; ++f) {
+                float s = part[f];
+                for (int q = 1; q < slices; ++q) s += part[(int64_t)q * count + f];
+                y[f] = s;
             }
         }
+    }
+}
+
+struct GemmPlan {
+    int nm, nn, slices, gps;
+    int64_t wgs;
+};
+
+static GemmPlan gemm_plan(int64_t n, int64_t out, int64_t in) {
+    const Layout L(out, in);
+    GemmPlan p;
+    p.nm = (int)((n + kGemmBM - 1) / kGemmBM);
+    p.nn = (int)((out + kGemmBN - 1) / kGemmBN);
+    const int64_t tiles = (int64_t)p.nm * p.nn;
+    // K slices while the workgroups still fit one pass over the compute
+    // units, each slice at least 8 groups, partial sums within the workspace
+    int s = 1;
+    while (tiles * (s + 1) <= kComputeUnits && L.g4 >= 8 * (s + 1) &&
+           (size_t)(s + 1) * n * out * sizeof(float) <= kWorkspaceBytes)
+        ++s;
+    p.gps = (int)((L.g4 + s - 1) / s);
+    p.slices = (int)((L.g4 + p.gps - 1) / p.gps);
+    p.wgs = tiles * p.slices;
+    return p;
+}
+
+size_t gemm_workspace_bytes(int64_t n, int64_t out, int64_t in) {
+    const GemmPlan p = gemm_plan(n, out, in);
+    return p.slices > 1 ? (size_t)p.slices * n * out * sizeof(float) : 0;
 }
 
 bool gemm_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     (void)x_f16;
-    const int64_t gy = (n + kGemmBM - 1) / kGemmBM;
-    const int64_t gx = (out + kGemmBN - 1) / kGemmBN;
-    return n >= 1 && out >= 1 && in >= 32 && gy <= 65535 && gx <= 0x7fffffff;
+    if (n < 1 || out < 1 || in < 32) return false;
+    if (n * out > 0x7fffffff || n * in > ((int64_t)1 << 40)) return false;
+    const GemmPlan p = gemm_plan(n, out, in);
+    return p.wgs <= 0x7fffffff && gemm_workspace_bytes(n, out, in) <= kWorkspaceBytes;
 }
 
 hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y, int64_t n,
-                       int64_t out, int64_t in, hipStream_t stream) {
-    const dim3 grid((unsigned)((out + kGemmBN - 1) / kGemmBN), (unsigned)((n + kGemmBM - 1) / kGemmBM));
-    const dim3 block(kGemmWaves * 64);
+                       int64_t out, int64_t in, void *ws, hipStream_t stream) {
+    const Layout L(out, in);
+    const GemmPlan p = gemm_plan(n, out, in);
+    GemmArgs a;
+    a.packed = (const uint8_t *)packed;
+    a.x = x;
+    a.y = y;
+    a.part = p.slices > 1 ? (float *)ws : nullptr;
+    a.code_base = L.scale_bytes();
+    a.n = (int)n;
+    a.out = (int)out;
+    a.in = (int)in;
+    a.g4 = (int)L.g4;
+    a.tiles = (int)L.tiles;
+    a.nm = p.nm;
+    a.nn = p.nn;
+    a.slices = p.slices;
+    a.gps = p.gps;
+    a.die_map = (p.wgs % kDies == 0) ? 1 : 0;
+    const dim3 grid((unsigned)p.wgs), block(kGemmWaves * 64);
+    const size_t lds = (size_t)kGemmLds;
     if (x_f16)
-        hipLaunchKernelGGL(gemm_kernel<_Float16>, grid, block, 0, stream, (const uint8_t *)packed,
-                           (const _Float16 *)x, y, n, out, in);
+        hipLaunchKernelGGL(gemm_kernel<_Float16>, grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL(gemm_kernel<float>, grid, block, 0, stream, (const uint8_t *)packed,
-                           (const float *)x, y, n, out, in);
+        hipLaunchKernelGGL(gemm_kernel<float>, grid, block, lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.slices == 1) return e;
+    const int64_t count = n * out;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)grid_for((count + 3) / 4, 256)),
+                       dim3(256), 0, stream, (const float *)a.part, y, count, p.slices);
     return hipGetLastError();
 }
 

@@ -41,9 +41,11 @@ hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float 
                             int64_t n, int64_t out, int64_t in, void *ws,
                             hipStream_t stream);
 
-// Prefill kernel: binary16 MFMA on d * (q - 8) rounded to binary16.
+// Prefill kernel: binary16 MFMA on d * (q - 8) rounded to binary16.  When the
+// tiles cannot fill the device it splits K and needs the workspace.
 bool gemm_supports(int64_t n, int64_t out, int64_t in, int x_f16);
+size_t gemm_workspace_bytes(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y,
-                       int64_t n, int64_t out, int64_t in, hipStream_t stream);
+                       int64_t n, int64_t out, int64_t in, void *ws, hipStream_t stream);
 
 }  // namespace q4

@@ -202,7 +202,9 @@ def test_runs_on_a_side_stream():
 
 # ------------------------------------------------------------------ prefill
 @pytest.mark.parametrize("n,out,in_", [(9, 100, 96), (64, 256, 128), (100, 300, 160),
-                                       (130, 1000, 1056), (512, 1024, 1024)])
+                                       (130, 1000, 1056), (512, 1024, 1024),
+                                       # few tiles, long K: the K range is split
+                                       (200, 300, 4096), (33, 130, 9728)])
 @pytest.mark.parametrize("xdt", [np.float16, np.float32], ids=["xf16", "xf32"])
 def test_gemm_parity_small(n, out, in_, xdt):
     blk = synth.make_blocks(out, in_, seed=n + out)
