@@ -30,9 +30,10 @@
 //      value is exact q - 8 times d, rounded once to binary16.
 //   D: lane l holds weight row l%32 and activation rows 8(i/4) + 4h + i%4.
 //
-// Work split: workgroups are (M block, N block, K slice).  When the tiles
-// alone cannot fill the device the K range is cut into S slices whose
-// partial sums go to a workspace; a second kernel adds them in slice order.
+// Work split: whole 128 x 128 tiles for every full pass over the 256 compute
+// units; the tiles of the last, partial pass are cut along K into slices
+// that spread over all compute units, their partial tiles parked in a
+// workspace and added in slice order by a second kernel (deterministic).
 // Consecutive workgroup ids are dealt to the eight dies in turn; the ids are
 // permuted so that each die takes a contiguous run of tiles in which the M
 // blocks of one N block are adjacent, and its L2 serves their shared words.
@@ -69,13 +70,14 @@ struct GemmArgs {
     const uint8_t *packed;
     const void *x;
     float *y;
-    float *part;          // S partial products, S x n x out, when S > 1
+    float *part;          // partial tiles of the split work, 128 x 128 each
     int64_t code_base;    // byte offset of the code stream
     int n, out, in;
     int g4, tiles;        // layout: groups per row, 16-row tiles
-    int nm, nn, slices;   // M blocks, N blocks, K slices
-    int gps;              // groups per K slice
-    int die_map;          // permute ids per die
+    int nm, nn;           // M blocks, N blocks (tile t: M block t % nm, N block t / nm)
+    int full;             // tiles 0 .. full-1 are computed whole
+    int rem, split, gps;  // the rem other tiles: split K slices of gps groups each
+    int die_full, die_split;  // permute ids per die in each part
 };
 
 // 8 consecutive float32 activations (zeros when !ok), and their binary16 form
@@ -135,18 +137,31 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     const int h = lane >> 5, c = lane & 31;
     const Magic mg = pinned_magic();
 
-    // ---- which tile and K slice -------------------------------------------
-    int id = blockIdx.x;
-    const int total = a.nm * a.nn * a.slices;
-    if (a.die_map) id = (id % kDies) * (total / kDies) + id / kDies;
-    const int mb = id % a.nm;
-    const int rest = id / a.nm;
-    const int nb = rest % a.nn;
-    const int sl = rest / a.nn;
+    // ---- which tile and K range ---------------------------------------------
+    // Ids below `full` take whole tiles; the others take K slices of the
+    // remaining tiles (piece q = slice * rem + tile - full, so consecutive
+    // pieces share a slice of the weights).  Within each part, consecutive
+    // ids are dealt to the eight dies in turn; they are permuted so each die
+    // takes a contiguous run, whose tiles share weight words in its L2.
+    const int id = blockIdx.x;
+    int tile, gs0, gs1, piece = -1;
+    if (id < a.full) {
+        tile = a.die_full ? (id % kDies) * (a.full / kDies) + id / kDies : id;
+        gs0 = 0;
+        gs1 = a.g4;
+    } else {
+        const int np = a.rem * a.split;
+        int q = id - a.full;
+        if (a.die_split) q = (q % kDies) * (np / kDies) + q / kDies;
+        piece = q;
+        tile = a.full + q % a.rem;
+        gs0 = (q / a.rem) * a.gps;
+        gs1 = gs0 + a.gps < a.g4 ? gs0 + a.gps : a.g4;
+    }
+    const int mb = tile % a.nm;
+    const int nb = tile / a.nm;
     const int wn = wave & 1, wk = wave >> 1;
     const int m0 = mb * kGemmBM;
-    const int gs0 = sl * a.gps;
-    const int gs1 = gs0 + a.gps < a.g4 ? gs0 + a.gps : a.g4;
     const int nsteps = gs1 - gs0;
     const XT *__restrict__ x = (const XT *)a.x;
 
@@ -360,15 +375,18 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
         constexpr bool PART = decltype(part_t)::value;
         constexpr bool NEXT = decltype(next_t)::value;
         if constexpr (REQ && !kDma) fetch(st + kStages - 1);
+        // The copies open each region: inline assembly is a scheduling
+        // boundary, so copies placed between the products and the operand
+        // work would keep the two from interleaving.
 #pragma unroll
         for (int kq = 0; kq < 3; ++kq) {
             const int cur = kq & 1;
+            if (REQ) fill(st + kStages - 1, kq, PART);
             products(cur);
             read_a(st, kq + 1, A[cur ^ 1]);
             if (kq == 1) spread(1);
             B[cur ^ 1][0] = frag(kq != 1, 0);
             B[cur ^ 1][1] = frag(kq != 1, 1);
-            if (REQ) fill(st + kStages - 1, kq, PART);
             interleave();
         }
         if constexpr (NEXT) {
@@ -377,10 +395,24 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
             Q4_WAIT_LGKM0();
             __builtin_amdgcn_s_barrier();
         }
-        products(1);
         if (REQ) fill(st + kStages - 1, 3, PART);
-        if constexpr (NEXT) prep_first(st + 1);
-        interleave();
+        products(1);
+        if constexpr (NEXT) {
+            // next step's weight words first, two products while they
+            // travel, then the decode between the remaining products
+            prep_first(st + 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);      // DS read: words, scales
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: A
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            interleave();
+        }
         if constexpr (REQ && !kDma) park(st + kStages - 1);
     };
 
@@ -424,7 +456,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     // tile back; then all four waves store whole rows, 16 bytes per lane.
     // Reads before writes: the compiler keeps LDS accesses that may alias in
     // program order, so interleaving them would serialize on LDS latency.
-    float *tile = reinterpret_cast<float *>(lds);            // 128 x 136 floats
+    float *ttile = reinterpret_cast<float *>(lds);           // 128 x 136 floats
     // lane holds tile column 64 wn + 32 ni + c, tile rows
     // 32 mi + 8 (v / 4) + 4 h + v % 4
     auto tix = [&](int mi, int ni, int v) {
@@ -436,7 +468,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) tile[tix(mi, ni, v)] = acc[mi][ni][v];
+                for (int v = 0; v < 16; ++v) ttile[tix(mi, ni, v)] = acc[mi][ni][v];
     }
     Q4_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
@@ -447,26 +479,37 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) other[mi][ni][v] = tile[tix(mi, ni, v)];
+                for (int v = 0; v < 16; ++v) other[mi][ni][v] = ttile[tix(mi, ni, v)];
 #pragma unroll
         for (int mi = 0; mi < kGemmMSub; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) tile[tix(mi, ni, v)] = acc[mi][ni][v] + other[mi][ni][v];
+                for (int v = 0; v < 16; ++v) ttile[tix(mi, ni, v)] = acc[mi][ni][v] + other[mi][ni][v];
     }
     Q4_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
-    float *dst = a.slices > 1 ? a.part + (int64_t)sl * a.n * a.out : a.y;
     const int n0 = nb * kGemmBN;
+    if (piece >= 0) {
+        // a K slice: the whole 128 x 128 partial tile, row-major, to the workspace
+        float *dst = a.part + (int64_t)piece * kGemmBM * kGemmBN;
+#pragma unroll 4
+        for (int it = 0; it < kGemmBM * kGemmBN / 4 / (kGemmWaves * 64); ++it) {
+            const int e = it * kGemmWaves * 64 + tid;          // float4 index in the tile
+            const int row = e >> 5, col = (e & 31) * 4;
+            *reinterpret_cast<float4 *>(dst + row * kGemmBN + col) =
+                *reinterpret_cast<const float4 *>(ttile + row * kTileStride + col);
+        }
+        return;
+    }
     const bool full_cols = n0 + kGemmBN <= a.out && (a.out & 3) == 0;
 #pragma unroll 4
     for (int it = 0; it < kGemmBM * kGemmBN / 4 / (kGemmWaves * 64); ++it) {
         const int e = it * kGemmWaves * 64 + tid;              // float4 index in the tile
         const int row = e >> 5, col = (e & 31) * 4;
         if (m0 + row >= a.n) continue;
-        const float4 v = *reinterpret_cast<const float4 *>(tile + row * kTileStride + col);
-        float *yp = dst + (int64_t)(m0 + row) * a.out + n0 + col;
+        const float4 v = *reinterpret_cast<const float4 *>(ttile + row * kTileStride + col);
+        float *yp = a.y + (int64_t)(m0 + row) * a.out + n0 + col;
         if (full_cols) {
             *reinterpret_cast<float4 *>(yp) = v;
         } else {
@@ -478,31 +521,43 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     }
 }
 
-// y = sum over the S slices of the partial products, in slice order.
+// y of the split tiles = sum of their K slices' partial tiles, in slice order.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ part,
-                                                          float *__restrict__ y, int64_t count,
-                                                          int slices) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
-    for (int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; e < count; e += stride) {
-        if (e + 4 <= count) {
-            float4 s = *reinterpret_cast<const float4 *>(part + e);
-            for (int q = 1; q < slices; ++q) {
-                const float4 t = *reinterpret_cast<const float4 *>(part + (int64_t)q * count + e);
-                s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-            }
-            *reinterpret_cast<float4 *>(y + e) = s;
+                                                          float *__restrict__ y, int n, int out,
+                                                          int nm, int full, int rem, int split) {
+    const int64_t count = (int64_t)rem * kGemmBM * kGemmBN / 4;   // float4 items
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += stride) {
+        const int r = (int)(e / (kGemmBM * kGemmBN / 4));
+        const int local = (int)(e % (kGemmBM * kGemmBN / 4)) * 4;
+        const int row = local / kGemmBN, col = local % kGemmBN;
+        const int t = full + r;
+        const int grow = (t % nm) * kGemmBM + row, gcol = (t / nm) * kGemmBN + col;
+        if (grow >= n) continue;
+        float4 s4 = *reinterpret_cast<const float4 *>(part + (int64_t)r * kGemmBM * kGemmBN + local);
+        for (int q = 1; q < split; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(
+                part + ((int64_t)q * rem + r) * kGemmBM * kGemmBN + local);
+            s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
+        }
+        float *yp = y + (int64_t)grow * out + gcol;
+        const float vv[4] = {s4.x, s4.y, s4.z, s4.w};
+        if (gcol + 4 <= out && (out & 3) == 0) {
+            *reinterpret_cast<float4 *>(yp) = s4;
         } else {
-            for (int64_t f = e; f < count; ++f) {
-                float s = part[f];
-                for (int q = 1; q < slices; ++q) s += part[(int64_t)q * count + f];
-                y[f] = s;
-            }
+            for (int q = 0; q < 4; ++q)
+                if (gcol + q < out) yp[q] = vv[q];
         }
     }
 }
 
+// Work split: whole tiles for as many full passes over the compute units as
+// the tile count allows; the remaining tiles (a partial pass) are cut along K
+// into as many slices as spread them over the compute units, each slice at
+// least kMinSliceGroups groups, and a second kernel adds the slices.
+constexpr int kMinSliceGroups = 4;
 struct GemmPlan {
-    int nm, nn, slices, gps;
+    int nm, nn, full, rem, split, gps;
     int64_t wgs;
 };
 
@@ -512,21 +567,28 @@ static GemmPlan gemm_plan(int64_t n, int64_t out, int64_t in) {
     p.nm = (int)((n + kGemmBM - 1) / kGemmBM);
     p.nn = (int)((out + kGemmBN - 1) / kGemmBN);
     const int64_t tiles = (int64_t)p.nm * p.nn;
-    // K slices while the workgroups still fit one pass over the compute
-    // units, each slice at least 8 groups, partial sums within the workspace
-    int s = 1;
-    while (tiles * (s + 1) <= kComputeUnits && L.g4 >= 8 * (s + 1) &&
-           (size_t)(s + 1) * n * out * sizeof(float) <= kWorkspaceBytes)
-        ++s;
-    p.gps = (int)((L.g4 + s - 1) / s);
-    p.slices = (int)((L.g4 + p.gps - 1) / p.gps);
-    p.wgs = tiles * p.slices;
+    const int64_t rem = tiles % kComputeUnits;
+    int64_t split = rem > 0 ? kComputeUnits / rem : 1;
+    const int64_t max_split = L.g4 / kMinSliceGroups;
+    if (split > max_split) split = max_split;
+    if (split < 2) {
+        p.full = (int)tiles;
+        p.rem = 0;
+        p.split = 1;
+        p.gps = (int)L.g4;
+    } else {
+        p.full = (int)(tiles - rem);
+        p.rem = (int)rem;
+        p.gps = (int)((L.g4 + split - 1) / split);
+        p.split = (int)((L.g4 + p.gps - 1) / p.gps);
+    }
+    p.wgs = (int64_t)p.full + (int64_t)p.rem * p.split;
     return p;
 }
 
 size_t gemm_workspace_bytes(int64_t n, int64_t out, int64_t in) {
     const GemmPlan p = gemm_plan(n, out, in);
-    return p.slices > 1 ? (size_t)p.slices * n * out * sizeof(float) : 0;
+    return (size_t)p.rem * p.split * kGemmBM * kGemmBN * sizeof(float);
 }
 
 bool gemm_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
@@ -545,7 +607,7 @@ hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y, i
     a.packed = (const uint8_t *)packed;
     a.x = x;
     a.y = y;
-    a.part = p.slices > 1 ? (float *)ws : nullptr;
+    a.part = p.rem > 0 ? (float *)ws : nullptr;
     a.code_base = L.scale_bytes();
     a.n = (int)n;
     a.out = (int)out;
@@ -554,9 +616,12 @@ hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y, i
     a.tiles = (int)L.tiles;
     a.nm = p.nm;
     a.nn = p.nn;
-    a.slices = p.slices;
+    a.full = p.full;
+    a.rem = p.rem;
+    a.split = p.split;
     a.gps = p.gps;
-    a.die_map = (p.wgs % kDies == 0) ? 1 : 0;
+    a.die_full = (p.full > 0 && p.full % kDies == 0) ? 1 : 0;
+    a.die_split = (p.rem > 0 && (p.rem * p.split) % kDies == 0) ? 1 : 0;
     const dim3 grid((unsigned)p.wgs), block(kGemmWaves * 64);
     const size_t lds = (size_t)kGemmLds;
     if (x_f16)
@@ -564,10 +629,11 @@ hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y, i
     else
         hipLaunchKernelGGL(gemm_kernel<float>, grid, block, lds, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.slices == 1) return e;
-    const int64_t count = n * out;
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)grid_for((count + 3) / 4, 256)),
-                       dim3(256), 0, stream, (const float *)a.part, y, count, p.slices);
+    if (e != hipSuccess || p.rem == 0) return e;
+    const int64_t count = (int64_t)p.rem * kGemmBM * kGemmBN / 4;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)grid_for(count, 256)), dim3(256), 0,
+                       stream, (const float *)a.part, y, (int)n, (int)out, p.nm, p.full, p.rem,
+                       p.split);
     return hipGetLastError();
 }
 
