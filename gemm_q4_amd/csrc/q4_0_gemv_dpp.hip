@@ -102,8 +102,11 @@ __global__ __launch_bounds__(kDppThreads) void gemv_dpp_kernel(
             for (int i = 0; i < TQ; ++i) {
                 const int64_t t = tile0 + i;
                 if (j < ng && t < L.tiles) {
-                    c[k][i] = load_u4(packed + L.tile_codes(t) + (int64_t)j * kGroupCodeBytes + lane * 16);
-                    sc[k][i] = load_u2(packed + L.tile_scales(t) + (int64_t)j * kGroupScaleBytes + r * 8);
+                    // streamed once: non-temporal loads keep L2 for x
+                    c[k][i] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(
+                        packed + L.tile_codes(t) + (int64_t)j * kGroupCodeBytes + lane * 16));
+                    sc[k][i] = __builtin_nontemporal_load(reinterpret_cast<const u2_t *>(
+                        packed + L.tile_scales(t) + (int64_t)j * kGroupScaleBytes + r * 8));
                 } else {
                     c[k][i] = u4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
                     sc[k][i] = u2_t{0u, 0u};

@@ -44,7 +44,7 @@
 namespace q4 {
 
 #ifndef Q4_MFMA_TARGET_WGS
-#define Q4_MFMA_TARGET_WGS 2048      // about eight workgroups per compute unit
+#define Q4_MFMA_TARGET_WGS 1024      // about four workgroups per compute unit
 #endif
 #ifndef Q4_MFMA_LDS_BUDGET
 #define Q4_MFMA_LDS_BUDGET (56 * 1024)
@@ -54,6 +54,11 @@ constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
 // x items (8 values) a thread stages: budget / 32 bytes per item / 256 threads
 constexpr int kMaxItems = (int)(Q4_MFMA_LDS_BUDGET / 32 / 256);
+#ifndef Q4_MFMA_STAGE_ITEMS
+#define Q4_MFMA_STAGE_ITEMS 2
+#endif
+// x items a staging thread aims to hold (sets the number of staging waves)
+constexpr int kStageItems = Q4_MFMA_STAGE_ITEMS;
 // groups per wave a kernel instance holds in registers
 constexpr int kGpwSet[] = {2, 4, 5, 8, 10, 16};
 
@@ -85,9 +90,11 @@ struct MfmaArgs {
     int gps;             // groups per K slice
     int per;             // groups per wave (<= GPW)
     int tpw;             // tiles per workgroup
+    int sw;              // waves that stage x (the first sw); the others only stream weights
 };
 
 struct MfmaPlan {
+    int stagers;      // waves that stage x
     int waves;        // waves per workgroup
     int gpw;          // register capacity per wave (template bound), >= per
     int per;          // groups per wave
@@ -129,16 +136,21 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Mfm
     const int k0 = gs0 * 128;                                // first k of the slice
     const int kin = a.in - k0 < nbs * 32 ? a.in - k0 : nbs * 32;
     const int items = nbs * NT * 4;
+    // x is loaded and staged by the first a.sw waves only: the other waves
+    // request their weight words at once, and no x wait of a staging wave
+    // covers weight loads (the memory counter is per wave and in order)
+    const bool stager = wave < a.sw;
+    const int nstage = a.sw * 64;
     float xv[kMaxItems][8];
 #pragma unroll
     for (int ii = 0; ii < kMaxItems; ++ii) {
-        const int it = tid + ii * (int)blockDim.x;
+        const int it = tid + ii * nstage;
         const int gq = it & 3;
         const int t = (it >> 2) % NT;
         const int bl = (it >> 2) / NT;
 #pragma unroll
         for (int k = 0; k < 8; ++k) xv[ii][k] = 0.0f;
-        if (it < items && bl * 32 < kin) {
+        if (stager && it < items && bl * 32 < kin) {
             const XT *p = x + (int64_t)t * a.in + k0 + 32 * bl + 4 * gq;
             const float4 u = load_x4<XT>(p), v = load_x4<XT>(p + 16);
             xv[ii][0] = u.x; xv[ii][1] = u.y; xv[ii][2] = u.z; xv[ii][3] = u.w;
@@ -156,8 +168,10 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Mfm
     u2_t sw[GPW];
     auto load_group = [&](int t, int q) {
         const int64_t j = (int64_t)t * a.g4 + (q < ng ? q : 0);
-        cw[q] = load_u4(cbase + j * kGroupCodeBytes);
-        sw[q] = load_u2(sbase + j * kGroupScaleBytes);
+        // read once per call: non-temporal, so the stream does not evict x
+        // and the other workgroups' lines from L2
+        cw[q] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(cbase + j * kGroupCodeBytes));
+        sw[q] = __builtin_nontemporal_load(reinterpret_cast<const u2_t *>(sbase + j * kGroupScaleBytes));
     };
 #pragma unroll
     for (int q = 0; q < GPW; ++q) load_group(tb, q);
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Mfm
     for (int t = 0; t < NT; ++t) mloc[t] = 0.0f;
 #pragma unroll
     for (int ii = 0; ii < kMaxItems; ++ii) {
-        const int it = tid + ii * (int)blockDim.x;
+        const int it = tid + ii * nstage;
         const int t = (it >> 2) % NT;
         float m = 0.0f;
 #pragma unroll
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Mfm
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         float m = 0.0f;
-        for (int w = 0; w < nwaves; ++w) m = fmaxf(m, rowmax[w][t]);
+        for (int w = 0; w < a.sw; ++w) m = fmaxf(m, rowmax[w][t]);
         // largest |x| of the row lands in [2^14, 2^15)
         scale[t] = 1.0f;
         if (m > 0.0f && m <= 3.0e38f) {
@@ -203,8 +217,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Mfm
     }
 #pragma unroll
     for (int ii = 0; ii < kMaxItems; ++ii) {
-        const int it = tid + ii * (int)blockDim.x;
-        if (it < items) {
+        const int it = tid + ii * nstage;
+        if (stager && it < items) {
             const int gq = it & 3;
             const int t = (it >> 2) % NT;
             const int bl = (it >> 2) / NT;
@@ -355,6 +369,10 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     p.gpw = 0;
     for (int v : kGpwSet)
         if (p.gpw == 0 && v >= p.per) p.gpw = v;
+    // staging waves: as few as hold the slice's x items in registers
+    p.stagers = (int)((items + kStageItems * 64 - 1) / (kStageItems * 64));
+    if (p.stagers < 1) p.stagers = 1;
+    if (p.stagers > p.waves) p.stagers = p.waves;
     // about kMfmaTargetWgs workgroups in all, each walking a run of tiles
     int64_t tpw = (L.tiles * p.slices + kMfmaTargetWgs - 1) / kMfmaTargetWgs;
     if (tpw < 1) tpw = 1;
@@ -377,7 +395,7 @@ bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (p.gpw == 0 || p.waves > kMfmaMaxWaves || p.slices > 65535 || p.gx > 0x7fffffff)
         return false;
     if ((int64_t)p.waves * p.per < p.gps) return false;
-    if (p.gps * 4 * n * 4 > (int64_t)kMaxItems * p.waves * 64) return false;
+    if (p.gps * 4 * n * 4 > (int64_t)kMaxItems * p.stagers * 64) return false;
     return gemv_mfma_workspace_bytes(n, out, in) <= kWorkspaceBytes;
 }
 
@@ -399,6 +417,7 @@ static hipError_t launch_mfma_t(const void *packed, const void *x, float *y, int
     a.gps = (int)p.gps;
     a.per = p.per;
     a.tpw = (int)p.tpw;
+    a.sw = p.stagers;
     const dim3 gd((unsigned)p.gx, (unsigned)p.slices), bd(p.waves * 64);
     const size_t lds = (size_t)mfma_lds_bytes(NT, p.gps);
     switch (p.gpw) {
