@@ -22,7 +22,8 @@ import os
 import torch  # noqa: F401  (must precede the CDLL below)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libq4_0.so")
+# Q4_0_LIBRARY names another build of the same library (a tuning variant)
+LIB_PATH = os.environ.get("Q4_0_LIBRARY") or os.path.join(_HERE, "libq4_0.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -74,6 +75,7 @@ _SIGS = {
     "q4_0_strerror": (ctypes.c_char_p, [_int]),
     "q4_0_version": (_int, []),
     "q4_0_release_workspaces": (_int, []),
+    "q4_0_matmul_grouped": (_int, [_vp, _int, _int, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -152,6 +154,25 @@ def q4_0_matmul_ex(packed, x, x_dtype: int, y, n: int, out: int, in_: int,
     _check(_lib.q4_0_matmul_ex(_ptr(packed), _ptr(x), x_dtype, _ptr(y), n, out,
                                in_, kernel, _stream(stream, packed, x, y)),
            "q4_0_matmul_ex")
+
+
+class q4_0_linear(ctypes.Structure):
+    """One linear of q4_0_matmul_grouped (struct q4_0_linear of include/q4_0.h)."""
+    _fields_ = [("packed", _vp), ("x", _vp), ("y", _vp), ("out", _i64), ("in_", _i64)]
+
+
+MAX_GROUP = 8
+
+
+def q4_0_matmul_grouped(linears, x_dtype: int, n: int, stream=None) -> None:
+    """linears: sequence of (packed, x, y, out, in) with tensors or pointers."""
+    arr = (q4_0_linear * max(1, len(linears)))()
+    tensors = []
+    for i, (packed, x, y, out, in_) in enumerate(linears):
+        arr[i] = q4_0_linear(_ptr(packed), _ptr(x), _ptr(y), out, in_)
+        tensors += [packed, x, y]
+    _check(_lib.q4_0_matmul_grouped(ctypes.cast(arr, _vp), len(linears), x_dtype, n,
+                                    _stream(stream, *tensors)), "q4_0_matmul_grouped")
 
 
 def q4_0_select_kernel(n: int, out: int, in_: int, x_dtype: int = F32) -> int:

@@ -5,7 +5,7 @@
 #include <mutex>
 #include <utility>
 
-#include "../../include/q4_0.h"
+#include "q4_0.h"
 #include "q4_0_internal.h"
 
 namespace {
@@ -162,6 +162,55 @@ int q4_0_matmul_ex(const void *packed, const void *x, int x_dtype, float *y, int
 int q4_0_matmul(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
                 int64_t out, int64_t in, void *stream) {
     return q4_0_matmul_ex(packed, x, x_dtype, y, n, out, in, Q4_0_KERNEL_AUTO, stream);
+}
+
+int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
+                        void *stream) {
+    if (!linears) return Q4_0_ENULL;
+    if (count < 1 || count > Q4_0_MAX_GROUP) return Q4_0_EINVAL;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    const int x_f16 = x_dtype == Q4_0_F16;
+    bool one_launch = true;
+    size_t ws_total = 0;
+    q4::GemvProblem probs[Q4_0_MAX_GROUP];
+    for (int i = 0; i < count; ++i) {
+        const q4_0_linear &L = linears[i];
+        const int st = check_shape(n, L.out, L.in);
+        if (st != Q4_0_OK) return st;
+        if (!L.packed || !L.x || !L.y) return Q4_0_ENULL;
+        if (!aligned(L.packed, 16) || !aligned(L.x, 16) || !aligned(L.y, 4)) return Q4_0_EALIGN;
+        const size_t ybytes = (size_t)n * (size_t)L.out * 4u;
+        for (int j = 0; j < count; ++j) {
+            const q4_0_linear &M = linears[j];
+            const size_t xb = (size_t)n * (size_t)M.in * (size_t)elem_bytes(x_dtype);
+            if (overlaps(L.y, ybytes, M.x, xb) ||
+                overlaps(L.y, ybytes, M.packed, q4_0_packed_bytes(M.out, M.in)))
+                return Q4_0_EALIAS;
+            if (j != i && overlaps(L.y, ybytes, M.y, (size_t)n * (size_t)M.out * 4u))
+                return Q4_0_EALIAS;
+        }
+        if (auto_kernel(n, L.out, L.in, x_f16) != Q4_0_KERNEL_GEMV_MFMA)
+            one_launch = false;
+        else
+            ws_total += q4::gemv_mfma_workspace_bytes(n, L.out, L.in);
+        probs[i] = {L.packed, L.x, L.y, L.out, L.in};
+    }
+    if (ws_total > q4::kWorkspaceBytes) one_launch = false;
+    const hipStream_t s = (hipStream_t)stream;
+    if (!one_launch) {
+        for (int i = 0; i < count; ++i) {
+            const q4_0_linear &L = linears[i];
+            const int st = q4_0_matmul(L.packed, L.x, x_dtype, L.y, n, L.out, L.in, stream);
+            if (st != Q4_0_OK) return st;
+        }
+        return Q4_0_OK;
+    }
+    void *ws = nullptr;
+    if (ws_total > 0) {
+        const int wst = get_workspace(s, &ws);
+        if (wst != Q4_0_OK) return wst;
+    }
+    return map_hip(q4::launch_gemv_mfma_group(probs, count, n, x_f16, ws, s));
 }
 
 const char *q4_0_strerror(int status) {

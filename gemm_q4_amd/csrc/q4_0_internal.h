@@ -35,11 +35,24 @@ hipError_t launch_gemv_dpp(const void *packed, const void *x, int x_f16, float *
 
 // Small-n MFMA kernel: activations split into binary16 high and low parts
 // (a 16-row MFMA A operand), weights decoded to exact q - 8 in binary16.
+// One launch can carry up to kMaxGroupLinears linears that share n and the
+// activation type; the workspace holds their K-split partial sums one after
+// another (each linear's share is gemv_mfma_workspace_bytes).
+constexpr int kMaxGroupLinears = 8;
+struct GemvProblem {
+    const void *packed;
+    const void *x;
+    float *y;
+    int64_t out, in;
+};
 bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16);
 size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in);
+int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y,
                             int64_t n, int64_t out, int64_t in, void *ws,
                             hipStream_t stream);
+hipError_t launch_gemv_mfma_group(const GemvProblem *probs, int count, int64_t n, int x_f16,
+                                  void *ws, hipStream_t stream);
 
 // Prefill kernel: binary16 MFMA on d * (q - 8) rounded to binary16.  When the
 // tiles cannot fill the device it splits K and needs the workspace.

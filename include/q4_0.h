@@ -127,6 +127,35 @@ int q4_0_matmul_ex(const void *packed, const void *x, int x_dtype, float *y,
                    int64_t n, int64_t out, int64_t in, int kernel,
                    void *stream);
 
+/* One linear of a group: y = x . W^T with the conventions of q4_0_matmul
+ * (packed: repacked W, 16-byte aligned; x: [n x in] row-major, 16-byte
+ * aligned; y: [n x out] float32, fully overwritten). */
+typedef struct q4_0_linear {
+    const void *packed;
+    const void *x;
+    float *y;
+    int64_t out, in;
+} q4_0_linear;
+
+#define Q4_0_MAX_GROUP 8
+
+/* Several linears that share n and the activation type, e.g. the Q, K and V
+ * projections of one input, or the gate and up projections of a feed-forward
+ * block.  golem README "Several conversations, one pass": one read of the
+ * weights carries every column of the batch; here one launch also carries
+ * every weight matrix of the group, so the per-launch cost and the tail of
+ * each launch are paid once.
+ *   linears : HOST array of `count` descriptors, 1 <= count <= Q4_0_MAX_GROUP;
+ *             each is checked as q4_0_matmul checks its arguments.
+ *   No y may overlap any x, any packed W or another y of the group
+ *   (Q4_0_EALIAS).  The x of different linears may be the same buffer.
+ * When the small-n MFMA kernel takes every linear (n <= 8) the group runs as
+ * one launch (plus one reduction launch if a linear splits K); otherwise
+ * each linear runs as q4_0_matmul would, in array order.  Results equal those
+ * of q4_0_matmul on each linear alone, bit for bit. */
+int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
+                        void *stream);
+
 /* The kernel q4_0_matmul would run for this call shape (a Q4_0_KERNEL_*
  * value), or a negative status for an invalid shape.  Host only. */
 int q4_0_select_kernel(int64_t n, int64_t out, int64_t in, int x_dtype);

@@ -158,3 +158,25 @@ def test_strerror_covers_every_status():
         assert q4.q4_0_strerror(st) != "unknown status"
     assert q4.q4_0_strerror(-99) == "unknown status"
     assert q4.q4_0_version() >= 100
+
+
+def test_grouped_validation():
+    grp = q4.q4_0_matmul_grouped
+    lin = (A16, B16, C16, 10, 64)
+    assert status_of(grp, [], q4.F32, 1) == q4.EINVAL                 # count 0
+    assert status_of(grp, [lin] * (q4.MAX_GROUP + 1), q4.F32, 1) == q4.EINVAL
+    assert status_of(grp, [lin], 7, 1) == q4.EINVAL                   # dtype
+    assert status_of(grp, [(A16, B16, C16, 10, 48)], q4.F32, 1) == q4.ESHAPE
+    assert status_of(grp, [lin], q4.F32, 0) == q4.ESHAPE
+    assert status_of(grp, [(0, B16, C16, 10, 64)], q4.F32, 1) == q4.ENULL
+    assert status_of(grp, [(A16, B16, 0, 10, 64)], q4.F32, 1) == q4.ENULL
+    assert status_of(grp, [(A16 + 8, B16, C16, 10, 64)], q4.F32, 1) == q4.EALIGN
+    # the second linear's x lies inside the first linear's y
+    other = (A16 + (1 << 16), C16 + 16, C16 + (1 << 20), 10, 64)
+    assert status_of(grp, [lin, other], q4.F32, 1) == q4.EALIAS
+    # two outputs overlap
+    other = (A16 + (1 << 16), B16, C16 + 8, 10, 64)
+    assert status_of(grp, [lin, other], q4.F32, 1) == q4.EALIAS
+    # one y inside another linear's packed weights
+    other = (C16 - 16, B16, C16 + (1 << 20), 10, 64)
+    assert status_of(grp, [lin, other], q4.F32, 1) == q4.EALIAS

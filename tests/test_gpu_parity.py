@@ -90,6 +90,68 @@ def test_block_decode_all_linears_auto(n):
         assert r <= TOL_SMALL_N, (lin.name, n, r)
 
 
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_grouped_block_equals_single_calls_and_oracle(n):
+    """The 7 linears of a 4B-class block in one grouped launch: each y equals
+    the single-linear result and matches the oracle."""
+    wl = synth.WORKLOADS["block_decode"]
+    lins, singles, blocks, xs = [], [], [], []
+    for i, lin in enumerate(wl.linears):
+        blk = synth.make_blocks(lin.out, lin.in_, seed=synth.seed_for(wl.name, i))
+        x = synth.make_x(n, lin.in_, seed=200 + i)
+        p = packed_from_blocks(blk, lin.out, lin.in_)
+        xd = to_dev(x)
+        y = torch.full((n, lin.out), float("nan"), device=DEV)
+        lins.append((p, xd, y, lin.out, lin.in_))
+        singles.append(run(p, x, lin.out))
+        blocks.append(blk)
+        xs.append(x)
+    q4.q4_0_matmul_grouped(lins, q4.F32, n)
+    torch.cuda.synchronize()
+    for i, lin in enumerate(wl.linears):
+        y = lins[i][2].cpu().numpy()
+        assert np.array_equal(y, singles[i]), lin.name
+        rows = np.arange(0, lin.out, 7)
+        assert ratio(y, blocks[i], xs[i], lin.out, lin.in_, rows=rows) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("n", [3, 8])
+def test_grouped_ragged_shapes_shared_x_and_k_split(n):
+    """Ragged rows, a partial last group, one x shared by several linears, and
+    K-split linears (n = 8 at in = 4128) next to unsplit ones in one launch."""
+    shapes = [(37, 4128), (16, 4128), (1, 4128), (300, 4128), (5, 4128)]
+    x = synth.make_x(n, 4128, seed=9)
+    xd = to_dev(x)
+    lins, blocks = [], []
+    for i, (out, in_) in enumerate(shapes):
+        blk = synth.make_blocks(out, in_, seed=40 + i)
+        p = packed_from_blocks(blk, out, in_)
+        lins.append((p, xd, torch.full((n, out), float("nan"), device=DEV), out, in_))
+        blocks.append(blk)
+    q4.q4_0_matmul_grouped(lins, q4.F32, n)
+    torch.cuda.synchronize()
+    for (p, _, y, out, in_), blk in zip(lins, blocks):
+        yy = y.cpu().numpy()
+        assert np.array_equal(yy, run(p, x, out)), (out, in_)
+        assert ratio(yy, blk, x, out, in_) <= TOL_SMALL_N
+
+
+def test_grouped_prefill_runs_each_linear_with_the_gemm():
+    n = 64
+    x = synth.make_x(n, 256, seed=3, dtype=np.float16)
+    xd = to_dev(x)
+    lins, blocks = [], []
+    for i, out in enumerate([96, 160]):
+        blk = synth.make_blocks(out, 256, seed=60 + i)
+        lins.append((packed_from_blocks(blk, out, 256), xd,
+                     torch.empty((n, out), device=DEV), out, 256))
+        blocks.append(blk)
+    q4.q4_0_matmul_grouped(lins, q4.F16, n)
+    torch.cuda.synchronize()
+    for (p, _, y, out, in_), blk in zip(lins, blocks):
+        assert ratio(y.cpu().numpy(), blk, x, out, in_) <= TOL_GEMM
+
+
 @pytest.mark.parametrize("n", [1, 4])
 def test_logit_head_full(n):
     out, in_ = 151936, 2560
