@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--n", type=int, default=None, help="rows of x (decode workloads)")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "gemv_dpp", "gemv_mfma", "gemm"])
+    ap.add_argument("--grouped", action="store_true",
+                    help="block_decode: run the projections as grouped launches "
+                         "(Q,K,V | O | gate,up | down)")
     ap.add_argument("--quick", action="store_true",
                     help="headline workload only (no extra workloads, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -91,9 +94,18 @@ class Case:
 GRAPH_STEPS = 100   # steps recorded in one HIP graph
 
 
-def timed(torch, q4, cases, kernel, steps, warmup, graph=True):
+# The block's projections grouped as one decoder block runs them: Q, K and V
+# read the same input, so do gate and up; O and down each wait for the
+# previous step of the block.
+BLOCK_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
+def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None):
     """Time `steps` steps (each step = every case once, on its next weight
     copy) between two events on the launch stream; return ms per step.
+
+    With `groups` (lists of case indices) each group runs as one
+    q4_0_matmul_grouped call whose linears all read the group's first x.
 
     With graph=True the launches are recorded once in a HIP graph that walks
     every weight copy (a multiple of GRAPH_STEPS steps) and the graph is
@@ -102,11 +114,21 @@ def timed(torch, q4, cases, kernel, steps, warmup, graph=True):
     run them).  Returns (ms per step, steps actually timed)."""
     stream = torch.cuda.current_stream()
     ncopy = len(cases[0].packed)
+    for grp in groups or ():
+        for k in grp:
+            cases[k].x = cases[grp[0]].x      # the group reads one input
 
     def step(i, sh):
-        for c in cases:
-            q4.q4_0_matmul_ex(c.packed[i % ncopy], c.x, c.xcode, c.y, c.n, c.out,
-                              c.in_, kernel, sh)
+        if groups is None:
+            for c in cases:
+                q4.q4_0_matmul_ex(c.packed[i % ncopy], c.x, c.xcode, c.y, c.n, c.out,
+                                  c.in_, kernel, sh)
+            return
+        for grp in groups:
+            xg = cases[grp[0]].x
+            q4.q4_0_matmul_grouped(
+                [(cases[k].packed[i % ncopy], xg, cases[k].y, cases[k].out, cases[k].in_)
+                 for k in grp], cases[grp[0]].xcode, cases[grp[0]].n, sh)
 
     for i in range(warmup):
         step(i, stream.cuda_stream)
@@ -173,13 +195,14 @@ def traffic_for(workload, kernel_name):
     return ent.get("bytes_per_launch")
 
 
-def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup):
+def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, groups=None):
     total_w = sum(q4.q4_0_blocks_bytes(o, i) for o, i in linears)
     copies = copies_for(total_w)
     cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies)
              for k, (o, i) in enumerate(linears)]
-    ms, steps = timed(torch, q4, cases, kernel, steps, warmup)
-    ms_eager, _ = timed(torch, q4, cases, kernel, min(steps, 200), 5, graph=False)
+    ms, steps = timed(torch, q4, cases, kernel, steps, warmup, groups=groups)
+    ms_eager, _ = timed(torch, q4, cases, kernel, min(steps, 200), 5, graph=False,
+                        groups=groups)
     gbs = total_w / (ms * 1e-3) / 1e9
     kern = sorted({q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, o, i) if kernel == 0 else kernel]
                    for o, i in linears})
@@ -187,7 +210,8 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup):
            "ms_per_step_eager": round(ms_eager, 5),
            "weight_bytes": total_w, "GB/s": round(gbs, 1),
            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern,
-           "launches_per_step": len(linears), "rotation_copies": copies}
+           "launches_per_step": len(linears) if groups is None else len(groups),
+           "grouped": groups is not None, "rotation_copies": copies}
     del cases
     torch.cuda.empty_cache()
     return res
@@ -264,8 +288,13 @@ def main():
         copies = copies_for(total_w)
         cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies)
                  for k, (o, i) in enumerate(linears)]
-        ms, steps_done = timed(torch, q4, cases, kernel, args.steps, args.warmup)
-        ms_eager, _ = timed(torch, q4, cases, kernel, min(args.steps, 500), 5, graph=False)
+        groups = None
+        if args.grouped and args.workload == "block_decode":
+            names = [l.name for l in wl.linears]
+            groups = [[names.index(nm) for nm in grp] for grp in BLOCK_GROUPS]
+        ms, steps_done = timed(torch, q4, cases, kernel, args.steps, args.warmup, groups=groups)
+        ms_eager, _ = timed(torch, q4, cases, kernel, min(args.steps, 500), 5, graph=False,
+                            groups=groups)
         parity = max(parity_check(q4, __import__("oracle"), synth, c, seed=k)
                      for k, c in enumerate(cases))
         value = total_w / (ms * 1e-3) / 1e9
@@ -280,6 +309,7 @@ def main():
                "weight_bytes_per_step": total_w,
                "algorithmic_bytes_per_launch": per_launch_bytes,
                "timing": "HIP graph replay of the step's launches",
+               "grouped": groups is not None,
                "ms_per_step_eager": round(ms_eager, 6)}
         dtype = "f32"
         del cases
@@ -290,9 +320,14 @@ def main():
             extra["decode"].append(decode_line(torch, q4, synth, "gemv_1024", [(1024, 1024)], 1,
                                                kernel, 2000, 100))
             blk = [(l.out, l.in_) for l in synth.WORKLOADS["block_decode"].linears]
+            names = [l.name for l in synth.WORKLOADS["block_decode"].linears]
+            bgroups = [[names.index(nm) for nm in grp] for grp in BLOCK_GROUPS]
             for nn in (1, 2, 4, 8):
                 extra["decode"].append(decode_line(torch, q4, synth, "block_decode", blk, nn,
                                                    kernel, 300, 30))
+                if kernel == q4.KERNEL_AUTO:
+                    extra["decode"].append(decode_line(torch, q4, synth, "block_decode", blk,
+                                                       nn, kernel, 300, 30, groups=bgroups))
             for nn in (1, 4):
                 extra["decode"].append(decode_line(torch, q4, synth, "logit_head",
                                                    [(151936, 2560)], nn, kernel, 200, 20))

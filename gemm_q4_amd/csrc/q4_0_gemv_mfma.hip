@@ -66,6 +66,17 @@ constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
 // x items (8 values each) a lane holds while it stages: caps groups per wave x n
 constexpr int kMaxStageItems = 10;
+// Activation rows from which x is converted once per launch by a pre-pass
+// (xprep_kernel) instead of by every workgroup: measured on MI355X, the
+// per-workgroup conversion dominates a decode launch from a few rows on.
+#ifndef Q4_MFMA_PREP_MIN_N
+#define Q4_MFMA_PREP_MIN_N 4
+#endif
+constexpr int kPrepMinN = Q4_MFMA_PREP_MIN_N;
+// groups per wave when the A fragments of its range live in registers
+constexpr int kPrepMaxGroups = 5;
+// prepared fragments: per-row inverse scales (float) in the first 64 bytes
+constexpr int kFragHeader = 64;
 // tiles whose per-wave partial sums are parked before a workgroup reduction
 // (16 KB of LDS whatever n is)
 template <int NT> constexpr int red_tiles() { return 32 / NT < 2 ? 2 : 32 / NT; }
@@ -95,6 +106,7 @@ struct GemvLinear {
     const void *x;
     float *y;
     float *part;         // per-slice partial sums when K is split, else null
+    const uint8_t *frag; // x converted by xprep_kernel (prepared launches)
     int64_t code_base;   // byte offset of the code stream in `packed`
     int out, in;
     int g4, tiles;       // groups per padded row, 16-row tiles
@@ -121,12 +133,116 @@ struct MfmaPlan {
     int64_t lds;      // A-fragment bytes of one workgroup
 };
 
-// A-fragment store of one wave: for block bl of the wave's range, slot index
-// j in [0, 2*NT) (j < NT: high part of row j; j >= NT: low part of row
-// j - NT) and quarter g, 16 bytes at ((bl * 2*NT + j) * 4 + g) * 16, holding
-// the row's scaled values at k = 32*bl + 4g + {0, 2, 16, 18, 1, 3, 17, 19}
-// (the slot order of decode_word_pairs).
-template <int NT, typename XT, int GPW>
+// Scaled binary16 high and low parts of 8 activations, as two A fragments in
+// the slot order of decode_word_pairs: k = {0, 2, 16, 18, 1, 3, 17, 19} +
+// 4g of a block, from v[] = values at k = 4g + {0, 1, 2, 3, 16, 17, 18, 19}.
+__device__ __forceinline__ void split_fragment(const float v[8], float sc, h8_t &fh, h8_t &fl) {
+    _Float16 hi[8], lo[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float sv = v[k] * sc;
+        hi[k] = (_Float16)sv;
+        lo[k] = (_Float16)(sv - (float)hi[k]);
+    }
+    fh = h8_t{hi[0], hi[2], hi[4], hi[6], hi[1], hi[3], hi[5], hi[7]};
+    fl = h8_t{lo[0], lo[2], lo[4], lo[6], lo[1], lo[3], lo[5], lo[7]};
+}
+
+// Power-of-two scale that puts a row's largest |x| in [2^14, 2^15) (1 for a
+// zero or non-finite maximum), and its exact inverse.
+__device__ __forceinline__ float row_scale(float m) {
+    if (m > 0.0f && m <= 3.0e38f) {
+        const int e = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;
+        return pow2f(14 - e);
+    }
+    return 1.0f;
+}
+__device__ __forceinline__ float inverse_pow2(float sc) {
+    return pow2f(127 - (int)(__builtin_bit_cast(uint32_t, sc) >> 23));
+}
+
+// Pre-pass of a prepared launch: converts x [NT x in] once into the A
+// fragments every workgroup would otherwise build for itself.  Workgroup t
+// converts row t: item (block b, quarter g) holds the 8 values k = 32b + 4g +
+// {0..3, 16..19}; each thread loads its items (kPrepItems of them in
+// registers, more in further passes that load again), the workgroup finds
+// the row's largest |x|, and each item is written as slot j in [0, 2*NT)
+// (j < NT: high part of row j; j >= NT: low part of row j - NT) and quarter
+// g, 16 bytes at kFragHeader + ((b * 2*NT + j) * 4 + g) * 16.  Blocks past in
+// (up to the padded group) are zeros.  Float at byte 4t: the inverse of row
+// t's scale.  One memory round trip for rows up to 512 * kPrepItems / 4
+// blocks.
+constexpr int kPrepThreads = 512;
+constexpr int kPrepItems = 4;
+template <typename XT>
+__device__ __forceinline__ void load_item(const XT *row, int in, int it, float v[8]) {
+    const int b = it >> 2, gq = it & 3;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    if (b * 32 < in) {
+        const XT *p = row + 32 * b + 4 * gq;
+        const float4 u = load_x4<XT>(p), w = load_x4<XT>(p + 16);
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+        v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+    }
+}
+template <int NT, typename XT>
+__global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restrict__ x, int in,
+                                                             int nbpad,
+                                                             uint8_t *__restrict__ frag) {
+    __shared__ float wmax[kPrepThreads / 64];
+    const int t = blockIdx.x;
+    const XT *row = x + (int64_t)t * in;
+    const int items = nbpad * 4;
+    float v[kPrepItems][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPrepItems; ++i) {
+        const int it = threadIdx.x + i * kPrepThreads;
+        load_item(row, it < items ? in : 0, it, v[i]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[i][k]));
+    }
+    for (int it = threadIdx.x + kPrepItems * kPrepThreads; it < items; it += kPrepThreads) {
+        float w[8];
+        load_item(row, in, it, w);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(w[k]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kPrepThreads / 64; ++w) m = fmaxf(m, wmax[w]);
+    const float sc = row_scale(m);
+    if (threadIdx.x == 0) reinterpret_cast<float *>(frag)[t] = inverse_pow2(sc);
+    uint8_t *f = frag + kFragHeader;
+    auto store = [&](int it, const float w[8]) {
+        const int b = it >> 2, gq = it & 3;
+        h8_t fh, fl;
+        split_fragment(w, sc, fh, fl);
+        *reinterpret_cast<h8_t *>(f + ((b * 2 * NT + t) * 4 + gq) * 16) = fh;
+        *reinterpret_cast<h8_t *>(f + ((b * 2 * NT + NT + t) * 4 + gq) * 16) = fl;
+    };
+#pragma unroll
+    for (int i = 0; i < kPrepItems; ++i) {
+        const int it = threadIdx.x + i * kPrepThreads;
+        if (it < items) store(it, v[i]);
+    }
+    for (int it = threadIdx.x + kPrepItems * kPrepThreads; it < items; it += kPrepThreads) {
+        float w[8];
+        load_item(row, in, it, w);
+        store(it, w);
+    }
+}
+
+// A-fragment store of one wave (unprepared launches): for block bl of the
+// wave's range, slot j and quarter g as in xprep_kernel, 16 bytes at
+// ((bl * 2*NT + j) * 4 + g) * 16 of the wave's LDS region.  A prepared launch
+// loads each lane's own fragments of its range straight into registers.
+template <int NT, typename XT, int GPW, bool PREP>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const GemvArgs args) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int kRedTiles = red_tiles<NT>();
@@ -155,10 +271,31 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     const XT *__restrict__ x = (const XT *)a.x;
     const bool split = a.part != nullptr;
 
-    // ---- request this wave's range of x ---------------------------------------
+    // lane's A slot r: high part of row r (r < NT), low part of row r - 8
+    // (8 <= r < 8 + NT).  Lanes of unused slots read slot 0's fragment: a D
+    // row depends only on its own A row, and the rows of unused slots are
+    // never read, so their contents do not matter (they stay finite).
+    const int jslot = r < NT ? r : ((r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
+    constexpr int kBlockFrag = 2 * NT * 64;                   // fragment bytes per block
+    const int gw = ng > 0 ? gs0 + q0 : gs0;                   // first group of the wave
+
+    // ---- prepared launch: request this lane's fragments ------------------------
+    h8_t afr[PREP ? GPW : 1][4];
+    if constexpr (PREP) {
+        const uint8_t *fb = a.frag + kFragHeader + (jslot * 4 + g) * 16;
+#pragma unroll
+        for (int q = 0; q < GPW; ++q)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int64_t b = (int64_t)(gw + (q < ng ? q : 0)) * 4 + s4;
+                afr[q][s4] = *reinterpret_cast<const h8_t *>(fb + b * kBlockFrag);
+            }
+    }
+
+    // ---- otherwise request this wave's range of x -----------------------------
     // item = (block bl, row t, quarter gq): the 8 values k = 32bl + 4gq +
     // {0..3} and 32bl + 16 + 4gq + {0..3} of the wave's range.
-    constexpr int kItems = (GPW * 16 * NT + 63) / 64;         // per lane
+    constexpr int kItems = PREP ? 1 : (GPW * 16 * NT + 63) / 64;   // per lane
     static_assert(kItems <= kMaxStageItems, "x staging registers");
     const int kw0 = (gs0 + q0) * 128;                         // first k of the range
     const int kwn = ng == 0 ? 0 : (a.in - kw0 < ng * 128 ? a.in - kw0 : ng * 128);
@@ -172,7 +309,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
         const int bl = (it >> 2) / NT;
 #pragma unroll
         for (int k = 0; k < 8; ++k) xv[ii][k] = 0.0f;
-        if (it < items && bl * 32 < kwn) {
+        if (!PREP && it < items && bl * 32 < kwn) {
             const XT *p = x + (int64_t)t * a.in + kw0 + 32 * bl + 4 * gq;
             const float4 u = load_x4<XT>(p), v = load_x4<XT>(p + 16);
             xv[ii][0] = u.x; xv[ii][1] = u.y; xv[ii][2] = u.z; xv[ii][3] = u.w;
@@ -183,7 +320,6 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // ---- request the first tile's code and scale words --------------------
     // Group q of the wave is slice group q0 + q; a wave with fewer than GPW
     // groups (or none) repeats a valid address of its slice.
-    const int gw = ng > 0 ? gs0 + q0 : gs0;
     const uint8_t *cbase = a.packed + a.code_base + (int64_t)gw * kGroupCodeBytes + lane * 16;
     const uint8_t *sbase = a.packed + (int64_t)gw * kGroupScaleBytes + r * 8;
     u4_t cw[GPW];
@@ -205,6 +341,9 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // lanes, no LDS), then each lane scales its items, splits them into high
     // and low binary16 parts and writes them as fragments into the wave's own
     // LDS region.
+    float scale[NT];
+    uint8_t *frag = smem + wave * (a.per * 4 * kBlockFrag);
+    if constexpr (!PREP) {
     float mloc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) mloc[t] = 0.0f;
@@ -217,21 +356,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) mloc[tt] = t == tt ? fmaxf(mloc[tt], m) : mloc[tt];
     }
-    float scale[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         float m = mloc[t];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        // largest |x| of the row lands in [2^14, 2^15)
-        scale[t] = 1.0f;
-        if (m > 0.0f && m <= 3.0e38f) {
-            const int e = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;
-            scale[t] = pow2f(14 - e);
-        }
+        scale[t] = row_scale(m);
     }
-    constexpr int kBlockFrag = 2 * NT * 64;                   // fragment bytes per block
-    uint8_t *frag = smem + wave * (a.per * 4 * kBlockFrag);
 #pragma unroll
     for (int ii = 0; ii < kItems; ++ii) {
         const int it = lane + ii * 64;
@@ -242,16 +373,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             float sc = scale[0];
 #pragma unroll
             for (int tt = 1; tt < NT; ++tt) sc = t == tt ? scale[tt] : sc;
-            _Float16 hi[8], lo[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float sv = xv[ii][k] * sc;
-                hi[k] = (_Float16)sv;
-                lo[k] = (_Float16)(sv - (float)hi[k]);
-            }
-            // order k = {0, 2, 16, 18, 1, 3, 17, 19} (+4gq): v index {0,2,4,6,1,3,5,7}
-            const h8_t fh = h8_t{hi[0], hi[2], hi[4], hi[6], hi[1], hi[3], hi[5], hi[7]};
-            const h8_t fl = h8_t{lo[0], lo[2], lo[4], lo[6], lo[1], lo[3], lo[5], lo[7]};
+            h8_t fh, fl;
+            split_fragment(xv[ii], sc, fh, fl);
             *reinterpret_cast<h8_t *>(frag + ((bl * 2 * NT + t) * 4 + gq) * 16) = fh;
             *reinterpret_cast<h8_t *>(frag + ((bl * 2 * NT + NT + t) * 4 + gq) * 16) = fl;
         }
@@ -262,12 +385,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // lane's A slot r: high part of row r (r < NT), low part of row r - 8
-    // (8 <= r < 8 + NT).  Lanes of unused slots read slot 0's fragment: a D
-    // row depends only on its own A row, and the rows of unused slots are
-    // never read, so their contents do not matter (they stay finite).
-    const int jslot = r < NT ? r : ((r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
+    }
     const uint8_t *afrag = frag + (jslot * 4 + g) * 16;
     // D slots a lane can hold live: 4g+i for i < min(NT, 4)
     constexpr int kLive = NT < 4 ? NT : 4;
@@ -276,10 +394,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
 #pragma unroll
     for (int i = 0; i < kLive; ++i) {
         const int row = (4 * g + i) & 7;
-        float sc = 1.0f;
+        if constexpr (PREP) {
+            inv[i] = row < NT ? reinterpret_cast<const float *>(a.frag)[row] : 1.0f;
+        } else {
+            float sc = 1.0f;
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) sc = row == tt ? scale[tt] : sc;
-        inv[i] = pow2f(127 - (int)(__builtin_bit_cast(uint32_t, sc) >> 23));
+            for (int tt = 0; tt < NT; ++tt) sc = row == tt ? scale[tt] : sc;
+            inv[i] = inverse_pow2(sc);
+        }
     }
     const Magic mg = pinned_magic();
 
@@ -298,7 +420,11 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                 f4_t dd[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const h8_t av = *reinterpret_cast<const h8_t *>(ag + s * kBlockFrag);
+                    h8_t av;
+                    if constexpr (PREP)
+                        av = afr[q][s];
+                    else
+                        av = *reinterpret_cast<const h8_t *>(ag + s * kBlockFrag);
                     uint32_t qd[4];
                     decode_word_pairs(cw[q][s], mg, qd);
                     const f4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -401,23 +527,39 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
 
 static int64_t mfma_lds_bytes(int64_t n, int64_t groups) { return groups * 4 * 2 * n * 64; }
 
-static int gpw_for(int64_t per, int64_t n) {
+static int64_t round256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+// Bytes of the prepared fragments of an [n x in] x (header included).
+static int64_t frag_bytes(int64_t n, int64_t in) {
+    const Layout L(1, in);
+    return round256(kFragHeader + L.g4 * 4 * 2 * n * 64);
+}
+
+// Whether launches with n rows of x of width `in` use the pre-pass.
+static bool use_prep(int64_t n, int64_t in) {
+    return n >= kPrepMinN && frag_bytes(n, in) <= (int64_t)(kWorkspaceBytes / 4);
+}
+
+static int gpw_for(int64_t per, int64_t n, bool prep) {
     for (int v : kGpwSet)
-        if (v >= per && ((int64_t)v * 16 * n + 63) / 64 <= kMaxStageItems) return v;
+        if (v >= per && (prep || ((int64_t)v * 16 * n + 63) / 64 <= kMaxStageItems)) return v;
     return 0;
 }
 
 static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     const Layout L(out, in);
+    const bool prep = use_prep(n, in);
     MfmaPlan p;
-    // groups a wave may hold: the x it stages must fit its registers
-    int64_t per_cap = (kMaxStageItems * 64) / (16 * n);
+    // groups a wave may hold: the x it stages must fit its registers, or, when
+    // prepared, the A fragments of its range
+    int64_t per_cap = prep ? kPrepMaxGroups : (kMaxStageItems * 64) / (16 * n);
     if (per_cap > 16) per_cap = 16;
     if (per_cap < 1) per_cap = 1;     // n > 8: no plan can run (gemv_mfma_supports)
-    // slices: as few as keep the slice's A fragments within the LDS budget
-    // and the slice within the waves' capacity
-    int64_t gps_max = kMfmaLdsBudget / mfma_lds_bytes(n, 1);
-    if (gps_max > per_cap * kMfmaMaxWaves) gps_max = per_cap * kMfmaMaxWaves;
+    // slices: as few as keep the slice within the waves' capacity and, when
+    // x is staged in LDS, its A fragments within the LDS budget
+    int64_t gps_max = per_cap * kMfmaMaxWaves;
+    if (!prep && kMfmaLdsBudget / mfma_lds_bytes(n, 1) < gps_max)
+        gps_max = kMfmaLdsBudget / mfma_lds_bytes(n, 1);
     if (gps_max < 1) gps_max = 1;
     p.slices = (L.g4 + gps_max - 1) / gps_max;
     p.gps = (L.g4 + p.slices - 1) / p.slices;
@@ -430,25 +572,25 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     if (waves < 1) waves = 1;
     p.per = (int)((p.gps + waves - 1) / waves);
     p.waves = (int)((p.gps + p.per - 1) / p.per);
-    p.gpw = gpw_for(p.per, n);
+    p.gpw = gpw_for(p.per, n, prep);
     // about kMfmaTargetWgs workgroups in all, each walking a run of tiles
     int64_t tpw = (L.tiles * p.slices + kMfmaTargetWgs - 1) / kMfmaTargetWgs;
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
     p.gx = (L.tiles + tpw - 1) / tpw;
-    p.lds = (int64_t)p.waves * mfma_lds_bytes(n, p.per);
+    p.lds = prep ? 0 : (int64_t)p.waves * mfma_lds_bytes(n, p.per);
     return p;
 }
 
 static size_t mfma_part_bytes(const MfmaPlan &p, int64_t out, int64_t in) {
     if (p.slices == 1) return 0;
     const Layout L(out, in);
-    // whole 256-byte units, so each linear's partial sums of a group start aligned
-    return ((size_t)p.slices * (size_t)L.tiles * 8 * 16 * sizeof(float) + 255) & ~(size_t)255;
+    return (size_t)round256(p.slices * L.tiles * 8 * 16 * (int64_t)sizeof(float));
 }
 
 size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in) {
-    return mfma_part_bytes(mfma_plan(n, out, in), out, in);
+    const size_t part = mfma_part_bytes(mfma_plan(n, out, in), out, in);
+    return part + (use_prep(n, in) ? (size_t)frag_bytes(n, in) : 0);
 }
 
 bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
@@ -466,10 +608,30 @@ int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in) {
     return p.gx * p.slices;
 }
 
-template <int NT, typename XT, int GPW>
+template <int NT, typename XT, int GPW, bool PREP>
 static void launch_mfma_g(dim3 gd, dim3 bd, size_t lds, hipStream_t stream, const GemvArgs &a) {
-    if constexpr (((int64_t)GPW * 16 * NT + 63) / 64 <= kMaxStageItems)
-        hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW>), gd, bd, lds, stream, a);
+    if constexpr (PREP ? GPW <= kPrepMaxGroups
+                       : ((int64_t)GPW * 16 * NT + 63) / 64 <= kMaxStageItems)
+        hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW, PREP>), gd, bd, lds, stream, a);
+}
+
+template <int NT, typename XT, bool PREP>
+static hipError_t launch_mfma_p(int gpw, dim3 gd, dim3 bd, size_t lds, hipStream_t stream,
+                                const GemvArgs &a) {
+    switch (gpw) {
+    case 1: launch_mfma_g<NT, XT, 1, PREP>(gd, bd, lds, stream, a); break;
+    case 2: launch_mfma_g<NT, XT, 2, PREP>(gd, bd, lds, stream, a); break;
+    case 4: launch_mfma_g<NT, XT, 4, PREP>(gd, bd, lds, stream, a); break;
+    case 5: launch_mfma_g<NT, XT, 5, PREP>(gd, bd, lds, stream, a); break;
+    case 8: if (PREP) return hipErrorInvalidValue;
+            launch_mfma_g<NT, XT, 8, PREP>(gd, bd, lds, stream, a); break;
+    case 10: if (PREP) return hipErrorInvalidValue;
+             launch_mfma_g<NT, XT, 10, PREP>(gd, bd, lds, stream, a); break;
+    case 16: if (PREP) return hipErrorInvalidValue;
+             launch_mfma_g<NT, XT, 16, PREP>(gd, bd, lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int NT, typename XT>
@@ -478,7 +640,9 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
     GemvArgs a = {};
     ReduceArgs ra = {};
     int waves = 1, gpw = 0;
-    int64_t lds = 0, wg = 0, wsoff = 0;
+    int64_t wg = 0, wsoff = 0;
+    bool prep = true;
+    for (int i = 0; i < count; ++i) prep = prep && use_prep(NT, probs[i].in);
     for (int i = 0; i < count; ++i) {
         const GemvProblem &pr = probs[i];
         const MfmaPlan p = mfma_plan(NT, pr.out, pr.in);
@@ -488,6 +652,7 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         g.x = pr.x;
         g.y = pr.y;
         g.part = nullptr;
+        g.frag = nullptr;
         if (p.slices > 1) {
             g.part = (float *)((uint8_t *)ws + wsoff);
             ReduceLinear &rl = ra.lin[ra.nlin++];
@@ -513,29 +678,37 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         wg += p.gx * p.slices;
         if (p.waves > waves) waves = p.waves;
         if (p.gpw > gpw) gpw = p.gpw;
-        if (p.lds > lds) lds = p.lds;
     }
     a.nlin = count;
+    // prepared launch: one pre-pass per distinct x of the group, its
+    // fragments after the partial sums in the workspace
+    if (prep) {
+        for (int i = 0; i < count; ++i) {
+            for (int j = 0; j < i && !a.lin[i].frag; ++j)
+                if (probs[j].x == probs[i].x && probs[j].in == probs[i].in)
+                    a.lin[i].frag = a.lin[j].frag;
+            if (a.lin[i].frag) continue;
+            uint8_t *f = (uint8_t *)ws + wsoff;
+            a.lin[i].frag = f;
+            wsoff += frag_bytes(NT, probs[i].in);
+            const int nbpad = a.lin[i].g4 * 4;
+            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3(NT), dim3(kPrepThreads), 0, stream,
+                               (const XT *)probs[i].x, (int)probs[i].in, nbpad, f);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     // each wave's fragment region is laid out with its own linear's `per`;
     // the dynamic LDS covers the largest plan (waves x per x fragment bytes)
-    int64_t lds_all = 0;
-    for (int i = 0; i < count; ++i) {
-        const int64_t b = (int64_t)waves * mfma_lds_bytes(NT, a.lin[i].per);
-        if (b > lds_all) lds_all = b;
-    }
-    if (lds_all > lds) lds = lds_all;
+    int64_t lds = 0;
+    if (!prep)
+        for (int i = 0; i < count; ++i) {
+            const int64_t b = (int64_t)waves * mfma_lds_bytes(NT, a.lin[i].per);
+            if (b > lds) lds = b;
+        }
     const dim3 gd((unsigned)wg), bd(waves * 64);
-    switch (gpw) {
-    case 1: launch_mfma_g<NT, XT, 1>(gd, bd, (size_t)lds, stream, a); break;
-    case 2: launch_mfma_g<NT, XT, 2>(gd, bd, (size_t)lds, stream, a); break;
-    case 4: launch_mfma_g<NT, XT, 4>(gd, bd, (size_t)lds, stream, a); break;
-    case 5: launch_mfma_g<NT, XT, 5>(gd, bd, (size_t)lds, stream, a); break;
-    case 8: launch_mfma_g<NT, XT, 8>(gd, bd, (size_t)lds, stream, a); break;
-    case 10: launch_mfma_g<NT, XT, 10>(gd, bd, (size_t)lds, stream, a); break;
-    case 16: launch_mfma_g<NT, XT, 16>(gd, bd, (size_t)lds, stream, a); break;
-    default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
+                        : launch_mfma_p<NT, XT, false>(gpw, gd, bd, (size_t)lds, stream, a);
     if (e != hipSuccess || ra.nlin == 0) return e;
     hipLaunchKernelGGL((gemv_mfma_reduce_kernel<NT>), dim3((unsigned)grid_for(ra.total, 256)),
                        dim3(256), 0, stream, ra);
