@@ -19,14 +19,13 @@
  *    and enqueues its work only on `stream` (a hipStream_t; NULL is the null
  *    stream of the current device).  The current HIP device must be the one
  *    holding the buffers.
- *  - Device memory: shapes whose K is split across workgroups (on the
- *    small-n MFMA kernel, when n * in is too large for one workgroup's LDS)
- *    need a workspace for partial sums.  q4_0_matmul allocates it (32 MiB,
- *    hipMalloc) the first
- *    time such a shape runs on a (device, stream) pair and keeps it for later
- *    calls on that pair until q4_0_release_workspaces.  Run one call per
- *    stream before capturing that stream into a graph.  Nothing else is
- *    allocated.
+ *  - Device memory: some calls need a workspace: shapes whose K is split
+ *    across workgroups (partial sums), and small-n calls with n >= 4 (the
+ *    activations converted once into the matrix-core operand layout).
+ *    q4_0_matmul allocates it (32 MiB, hipMalloc) the first time such a call
+ *    runs on a (device, stream) pair and keeps it for later calls on that
+ *    pair until q4_0_release_workspaces.  Run one call per stream before
+ *    capturing that stream into a graph.  Nothing else is allocated.
  *  - Arguments are validated on the host before any HIP call; an invalid
  *    call returns a negative Q4_0_E* status and enqueues nothing.  Launch
  *    failures return Q4_0_EHIP.  Errors of work already enqueued (for
