@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--grouped", action="store_true",
                     help="block_decode: run the projections as grouped launches "
                          "(Q,K,V | O | gate,up | down)")
+    ap.add_argument("--argmax", action="store_true",
+                    help="decode workloads: q4_0_matmul_argmax with no y stored")
     ap.add_argument("--quick", action="store_true",
                     help="headline workload only (no extra workloads, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,12 +102,14 @@ GRAPH_STEPS = 100   # steps recorded in one HIP graph
 BLOCK_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
-def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None):
+def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None, argmax=False):
     """Time `steps` steps (each step = every case once, on its next weight
     copy) between two events on the launch stream; return ms per step.
 
     With `groups` (lists of case indices) each group runs as one
     q4_0_matmul_grouped call whose linears all read the group's first x.
+    With `argmax` each case runs as q4_0_matmul_argmax with no y stored (the
+    greedy pick of a logit head).
 
     With graph=True the launches are recorded once in a HIP graph that walks
     every weight copy (a multiple of GRAPH_STEPS steps) and the graph is
@@ -118,7 +122,17 @@ def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None):
         for k in grp:
             cases[k].x = cases[grp[0]].x      # the group reads one input
 
+    if argmax:
+        for c in cases:
+            c.mv = torch.empty(c.n, dtype=torch.float32, device="cuda")
+            c.mi = torch.empty(c.n, dtype=torch.int32, device="cuda")
+
     def step(i, sh):
+        if argmax:
+            for c in cases:
+                q4.q4_0_matmul_argmax(c.packed[i % ncopy], c.x, c.xcode, None, c.n, c.out,
+                                      c.in_, c.mv, c.mi, sh)
+            return
         if groups is None:
             for c in cases:
                 q4.q4_0_matmul_ex(c.packed[i % ncopy], c.x, c.xcode, c.y, c.n, c.out,
@@ -195,14 +209,15 @@ def traffic_for(workload, kernel_name):
     return ent.get("bytes_per_launch")
 
 
-def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, groups=None):
+def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, groups=None,
+                argmax=False):
     total_w = sum(q4.q4_0_blocks_bytes(o, i) for o, i in linears)
     copies = copies_for(total_w)
     cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies)
              for k, (o, i) in enumerate(linears)]
-    ms, steps = timed(torch, q4, cases, kernel, steps, warmup, groups=groups)
+    ms, steps = timed(torch, q4, cases, kernel, steps, warmup, groups=groups, argmax=argmax)
     ms_eager, _ = timed(torch, q4, cases, kernel, min(steps, 200), 5, graph=False,
-                        groups=groups)
+                        groups=groups, argmax=argmax)
     gbs = total_w / (ms * 1e-3) / 1e9
     kern = sorted({q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, o, i) if kernel == 0 else kernel]
                    for o, i in linears})
@@ -211,7 +226,7 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, group
            "weight_bytes": total_w, "GB/s": round(gbs, 1),
            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern,
            "launches_per_step": len(linears) if groups is None else len(groups),
-           "grouped": groups is not None, "rotation_copies": copies}
+           "grouped": groups is not None, "argmax": argmax, "rotation_copies": copies}
     del cases
     torch.cuda.empty_cache()
     return res
@@ -292,11 +307,12 @@ def main():
         if args.grouped and args.workload == "block_decode":
             names = [l.name for l in wl.linears]
             groups = [[names.index(nm) for nm in grp] for grp in BLOCK_GROUPS]
-        ms, steps_done = timed(torch, q4, cases, kernel, args.steps, args.warmup, groups=groups)
+        ms, steps_done = timed(torch, q4, cases, kernel, args.steps, args.warmup, groups=groups,
+                               argmax=args.argmax)
         ms_eager, _ = timed(torch, q4, cases, kernel, min(args.steps, 500), 5, graph=False,
-                            groups=groups)
-        parity = max(parity_check(q4, __import__("oracle"), synth, c, seed=k)
-                     for k, c in enumerate(cases))
+                            groups=groups, argmax=args.argmax)
+        parity = None if args.argmax else max(
+            parity_check(q4, __import__("oracle"), synth, c, seed=k) for k, c in enumerate(cases))
         value = total_w / (ms * 1e-3) / 1e9
         unit = "GB/s"
         kname = q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, *linears[0]) if kernel == 0 else kernel]
@@ -309,7 +325,7 @@ def main():
                "weight_bytes_per_step": total_w,
                "algorithmic_bytes_per_launch": per_launch_bytes,
                "timing": "HIP graph replay of the step's launches",
-               "grouped": groups is not None,
+               "grouped": groups is not None, "argmax": args.argmax,
                "ms_per_step_eager": round(ms_eager, 6)}
         dtype = "f32"
         del cases
@@ -331,6 +347,10 @@ def main():
             for nn in (1, 4):
                 extra["decode"].append(decode_line(torch, q4, synth, "logit_head",
                                                    [(151936, 2560)], nn, kernel, 200, 20))
+                if kernel == q4.KERNEL_AUTO:
+                    extra["decode"].append(decode_line(torch, q4, synth, "logit_head",
+                                                       [(151936, 2560)], nn, kernel, 200, 20,
+                                                       argmax=True))
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
 
     if args.calib_copy:

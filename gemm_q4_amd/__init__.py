@@ -76,6 +76,7 @@ _SIGS = {
     "q4_0_version": (_int, []),
     "q4_0_release_workspaces": (_int, []),
     "q4_0_matmul_grouped": (_int, [_vp, _int, _int, _i64, _vp]),
+    "q4_0_matmul_argmax": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -173,6 +174,24 @@ def q4_0_matmul_grouped(linears, x_dtype: int, n: int, stream=None) -> None:
         tensors += [packed, x, y]
     _check(_lib.q4_0_matmul_grouped(ctypes.cast(arr, _vp), len(linears), x_dtype, n,
                                     _stream(stream, *tensors)), "q4_0_matmul_grouped")
+
+
+def q4_0_matmul_argmax(packed, x, x_dtype: int, y, n: int, out: int, in_: int,
+                       max_val, max_idx, stream=None) -> None:
+    _check(_lib.q4_0_matmul_argmax(_ptr(packed), _ptr(x), x_dtype, _ptr(y), n, out, in_,
+                                   _ptr(max_val), _ptr(max_idx),
+                                   _stream(stream, packed, x, max_val)), "q4_0_matmul_argmax")
+
+
+def matmul_argmax(packed, x, out: int, y=None, stream=None):
+    """(max value [n] float32, max index [n] int32) of y = x . W^T per row;
+    y is written when given."""
+    import torch
+    n, in_ = x.shape
+    mv = torch.empty(n, dtype=torch.float32, device=x.device)
+    mi = torch.empty(n, dtype=torch.int32, device=x.device)
+    q4_0_matmul_argmax(packed, x, dtype_code(x), y, n, out, in_, mv, mi, stream)
+    return mv, mi
 
 
 def q4_0_select_kernel(n: int, out: int, in_: int, x_dtype: int = F32) -> int:

@@ -164,6 +164,40 @@ int q4_0_matmul(const void *packed, const void *x, int x_dtype, float *y, int64_
     return q4_0_matmul_ex(packed, x, x_dtype, y, n, out, in, Q4_0_KERNEL_AUTO, stream);
 }
 
+int q4_0_matmul_argmax(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
+                       int64_t out, int64_t in, float *max_val, int32_t *max_idx,
+                       void *stream) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    if (!packed || !x || !max_val || !max_idx) return Q4_0_ENULL;
+    if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(max_val, 4) ||
+        !aligned(max_idx, 4))
+        return Q4_0_EALIGN;
+    const size_t xbytes = (size_t)n * (size_t)in * (size_t)elem_bytes(x_dtype);
+    const size_t wbytes = q4_0_packed_bytes(out, in);
+    const size_t ybytes = y ? (size_t)n * (size_t)out * 4u : 0;
+    const size_t rbytes = (size_t)n * 4u;
+    const void *outs[3] = {y, max_val, max_idx};
+    const size_t olen[3] = {ybytes, rbytes, rbytes};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], olen[i], x, xbytes) || overlaps(outs[i], olen[i], packed, wbytes))
+            return Q4_0_EALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], olen[i], outs[j], olen[j])) return Q4_0_EALIAS;
+    }
+    const int x_f16 = x_dtype == Q4_0_F16;
+    if (!q4::gemv_mfma_supports(n, out, in, x_f16) ||
+        q4::gemv_mfma_argmax_workspace_bytes(n, out, in) > q4::kWorkspaceBytes)
+        return Q4_0_EUNSUPPORTED;
+    const hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    const int wst = get_workspace(s, &ws);
+    if (wst != Q4_0_OK) return wst;
+    return map_hip(q4::launch_gemv_mfma_argmax(packed, x, x_f16, y, n, out, in, max_val, max_idx,
+                                               ws, s));
+}
+
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream) {
     if (!linears) return Q4_0_ENULL;

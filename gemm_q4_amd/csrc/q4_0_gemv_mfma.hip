@@ -107,6 +107,7 @@ struct GemvLinear {
     float *y;
     float *part;         // per-slice partial sums when K is split, else null
     const uint8_t *frag; // x converted by xprep_kernel (prepared launches)
+    uint2 *amax;         // per-workgroup (max, index) of each row of y, or null
     int64_t code_base;   // byte offset of the code stream in `packed`
     int out, in;
     int g4, tiles;       // groups per padded row, 16-row tiles
@@ -159,6 +160,45 @@ __device__ __forceinline__ float row_scale(float m) {
 }
 __device__ __forceinline__ float inverse_pow2(float sc) {
     return pow2f(127 - (int)(__builtin_bit_cast(uint32_t, sc) >> 23));
+}
+
+// Running maximum of a row of y with its index: a larger value wins, an equal
+// value with a smaller index wins, a NaN never wins.
+__device__ __forceinline__ void amax_update(float v, int i, float &bv, int &bi) {
+    if (v > bv || (v == bv && i < bi)) {
+        bv = v;
+        bi = i;
+    }
+}
+
+// Workgroup-wide (max, index) of each of NT rows from every thread's
+// candidates; thread t < NT stores row t's pair at out[t] (value bits, index).
+// Called by every thread of the workgroup.
+template <int NT>
+__device__ void amax_workgroup(float (&bv)[NT], int (&bi)[NT], uint2 *out) {
+    __shared__ uint2 wb[kMfmaMaxWaves][NT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float v = bv[t];
+        int i = bi[t];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(v, off);
+            const int oi = __shfl_xor(i, off);
+            amax_update(ov, oi, v, i);
+        }
+        if (lane == 0) wb[wave][t] = uint2{__builtin_bit_cast(uint32_t, v), (uint32_t)i};
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < NT) {
+        const int t = threadIdx.x;
+        float v = -__builtin_huge_valf();
+        int i = 0x7fffffff;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w)
+            amax_update(__builtin_bit_cast(float, wb[w][t].x), (int)wb[w][t].y, v, i);
+        out[t] = uint2{__builtin_bit_cast(uint32_t, v), (uint32_t)i};
+    }
 }
 
 // Pre-pass of a prepared launch: converts x [NT x in] once into the A
@@ -270,6 +310,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     const int te = tb + a.tpw < a.tiles ? tb + a.tpw : a.tiles;
     const XT *__restrict__ x = (const XT *)a.x;
     const bool split = a.part != nullptr;
+    // running (max, index) of each row of y over this thread's outputs
+    float bv[NT];
+    int bi[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        bv[t] = -__builtin_huge_valf();
+        bi[t] = 0x7fffffff;
+    }
 
     // lane's A slot r: high part of row r (r < NT), low part of row r - 8
     // (8 <= r < 8 + NT).  Lanes of unused slots read slot 0's fragment: a D
@@ -466,7 +514,12 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             for (int w = 0; w < nwaves; ++w) sum += red[sl][w][tt][rr];
             if (!split) {
                 const int row = t * kTileRows + rr;
-                if (row < a.out) a.y[(int64_t)tt * a.out + row] = sum;
+                if (row < a.out) {
+                    if (a.y) a.y[(int64_t)tt * a.out + row] = sum;
+#pragma unroll
+                    for (int u = 0; u < NT; ++u)
+                        if (u == tt) amax_update(sum, row, bv[u], bi[u]);
+                }
             } else {
                 a.part[(((int64_t)sy * a.tiles + t) * 8 + tt) * 16 + rr] = sum;
             }
@@ -488,6 +541,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     }
     tile(t, t - t0, false);
     flush(t0, t - t0 + 1);
+    if (a.amax && !split) amax_workgroup<NT>(bv, bi, a.amax + (int64_t)local * NT);
 }
 
 // Sum of the parked per-tile sums over the S slices, in slice order, for
@@ -502,11 +556,19 @@ struct ReduceArgs {
     ReduceLinear lin[kMaxGroupLinears];
     int nlin;
     int64_t total;
+    uint2 *amax;         // per-workgroup (max, index) pairs of a single linear, or null
 };
 
 template <int NT>
 __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs args) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    float bv[NT];
+    int bi[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        bv[t] = -__builtin_huge_valf();
+        bi[t] = 0x7fffffff;
+    }
     for (int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; f < args.total;
          f += stride) {
         int li = 0;
@@ -521,7 +583,44 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
         for (int64_t q = 0; q < L.slices; ++q)
             s += L.part[((q * L.tiles + t) * 8 + tt) * 16 + rr];
         const int64_t row = t * kTileRows + rr;
-        if (row < L.out) L.y[(int64_t)tt * L.out + row] = s;
+        if (row < L.out) {
+            if (L.y) L.y[(int64_t)tt * L.out + row] = s;
+#pragma unroll
+            for (int u = 0; u < NT; ++u)
+                if (u == tt) amax_update(s, (int)row, bv[u], bi[u]);
+        }
+    }
+    if (args.amax) amax_workgroup<NT>(bv, bi, args.amax + (int64_t)blockIdx.x * NT);
+}
+
+// Final (max, index) of each row of y over `count` workgroup pairs; row t's
+// result in max_val[t], max_idx[t] (index -1 and a NaN value when no output
+// of the row is a number).
+template <int NT>
+__global__ __launch_bounds__(256) void amax_final_kernel(const uint2 *__restrict__ pairs,
+                                                         int count, float *max_val,
+                                                         int32_t *max_idx) {
+    float bv[NT];
+    int bi[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        bv[t] = -__builtin_huge_valf();
+        bi[t] = 0x7fffffff;
+    }
+    for (int k = threadIdx.x; k < count; k += blockDim.x)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint2 p = pairs[(int64_t)k * NT + t];
+            amax_update(__builtin_bit_cast(float, p.x), (int)p.y, bv[t], bi[t]);
+        }
+    __shared__ uint2 res[NT];
+    amax_workgroup<NT>(bv, bi, res);
+    __syncthreads();
+    if ((int)threadIdx.x < NT) {
+        const int t = threadIdx.x;
+        const bool none = (int)res[t].y == 0x7fffffff;
+        max_val[t] = none ? __builtin_nanf("") : __builtin_bit_cast(float, res[t].x);
+        max_idx[t] = none ? -1 : (int32_t)res[t].y;
     }
 }
 
@@ -588,9 +687,23 @@ static size_t mfma_part_bytes(const MfmaPlan &p, int64_t out, int64_t in) {
     return (size_t)round256(p.slices * L.tiles * 8 * 16 * (int64_t)sizeof(float));
 }
 
+// (max, index) pairs of an argmax launch: one per row per workgroup of the
+// kernel that finishes y (the product, or the K-slice reduction).
+static int64_t amax_pairs(const MfmaPlan &p, int64_t n, int64_t out, int64_t in) {
+    const Layout L(out, in);
+    const int64_t wgs = p.slices == 1 ? p.gx : grid_for(L.tiles * n * 16, 256);
+    return wgs * n;
+}
+
 size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in) {
     const size_t part = mfma_part_bytes(mfma_plan(n, out, in), out, in);
     return part + (use_prep(n, in) ? (size_t)frag_bytes(n, in) : 0);
+}
+
+size_t gemv_mfma_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
+    const MfmaPlan p = mfma_plan(n, out, in);
+    return gemv_mfma_workspace_bytes(n, out, in) +
+           (size_t)round256(amax_pairs(p, n, out, in) * (int64_t)sizeof(uint2));
 }
 
 bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
@@ -636,7 +749,7 @@ static hipError_t launch_mfma_p(int gpw, dim3 gd, dim3 bd, size_t lds, hipStream
 
 template <int NT, typename XT>
 static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
-                                hipStream_t stream) {
+                                hipStream_t stream, float *max_val, int32_t *max_idx) {
     GemvArgs a = {};
     ReduceArgs ra = {};
     int waves = 1, gpw = 0;
@@ -653,6 +766,7 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         g.y = pr.y;
         g.part = nullptr;
         g.frag = nullptr;
+        g.amax = nullptr;
         if (p.slices > 1) {
             g.part = (float *)((uint8_t *)ws + wsoff);
             ReduceLinear &rl = ra.lin[ra.nlin++];
@@ -706,27 +820,47 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             const int64_t b = (int64_t)waves * mfma_lds_bytes(NT, a.lin[i].per);
             if (b > lds) lds = b;
         }
+    // argmax of a single linear: (max, index) pairs after everything else
+    uint2 *pairs = nullptr;
+    int npairs = 0;
+    if (max_val) {
+        pairs = (uint2 *)((uint8_t *)ws + wsoff);
+        if (ra.nlin == 0) {
+            a.lin[0].amax = pairs;
+            npairs = a.lin[0].gx;
+        } else {
+            ra.amax = pairs;
+            npairs = (int)grid_for(ra.total, 256);
+        }
+    }
     const dim3 gd((unsigned)wg), bd(waves * 64);
     hipError_t e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
                         : launch_mfma_p<NT, XT, false>(gpw, gd, bd, (size_t)lds, stream, a);
-    if (e != hipSuccess || ra.nlin == 0) return e;
-    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<NT>), dim3((unsigned)grid_for(ra.total, 256)),
-                       dim3(256), 0, stream, ra);
+    if (e != hipSuccess) return e;
+    if (ra.nlin > 0) {
+        hipLaunchKernelGGL((gemv_mfma_reduce_kernel<NT>),
+                           dim3((unsigned)grid_for(ra.total, 256)), dim3(256), 0, stream, ra);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!max_val) return hipSuccess;
+    hipLaunchKernelGGL((amax_final_kernel<NT>), dim3(1), dim3(256), 0, stream,
+                       (const uint2 *)pairs, npairs, max_val, max_idx);
     return hipGetLastError();
 }
 
 template <typename XT>
 static hipError_t launch_mfma_x(const GemvProblem *probs, int count, int64_t n, void *ws,
-                                hipStream_t stream) {
+                                hipStream_t stream, float *mv, int32_t *mi) {
     switch (n) {
-    case 1: return launch_mfma_t<1, XT>(probs, count, ws, stream);
-    case 2: return launch_mfma_t<2, XT>(probs, count, ws, stream);
-    case 3: return launch_mfma_t<3, XT>(probs, count, ws, stream);
-    case 4: return launch_mfma_t<4, XT>(probs, count, ws, stream);
-    case 5: return launch_mfma_t<5, XT>(probs, count, ws, stream);
-    case 6: return launch_mfma_t<6, XT>(probs, count, ws, stream);
-    case 7: return launch_mfma_t<7, XT>(probs, count, ws, stream);
-    case 8: return launch_mfma_t<8, XT>(probs, count, ws, stream);
+    case 1: return launch_mfma_t<1, XT>(probs, count, ws, stream, mv, mi);
+    case 2: return launch_mfma_t<2, XT>(probs, count, ws, stream, mv, mi);
+    case 3: return launch_mfma_t<3, XT>(probs, count, ws, stream, mv, mi);
+    case 4: return launch_mfma_t<4, XT>(probs, count, ws, stream, mv, mi);
+    case 5: return launch_mfma_t<5, XT>(probs, count, ws, stream, mv, mi);
+    case 6: return launch_mfma_t<6, XT>(probs, count, ws, stream, mv, mi);
+    case 7: return launch_mfma_t<7, XT>(probs, count, ws, stream, mv, mi);
+    case 8: return launch_mfma_t<8, XT>(probs, count, ws, stream, mv, mi);
     default: return hipErrorInvalidValue;
     }
 }
@@ -734,8 +868,16 @@ static hipError_t launch_mfma_x(const GemvProblem *probs, int count, int64_t n, 
 hipError_t launch_gemv_mfma_group(const GemvProblem *probs, int count, int64_t n, int x_f16,
                                   void *ws, hipStream_t stream) {
     if (count < 1 || count > kMaxGroupLinears) return hipErrorInvalidValue;
-    return x_f16 ? launch_mfma_x<_Float16>(probs, count, n, ws, stream)
-                 : launch_mfma_x<float>(probs, count, n, ws, stream);
+    return x_f16 ? launch_mfma_x<_Float16>(probs, count, n, ws, stream, nullptr, nullptr)
+                 : launch_mfma_x<float>(probs, count, n, ws, stream, nullptr, nullptr);
+}
+
+hipError_t launch_gemv_mfma_argmax(const void *packed, const void *x, int x_f16, float *y,
+                                   int64_t n, int64_t out, int64_t in, float *max_val,
+                                   int32_t *max_idx, void *ws, hipStream_t stream) {
+    const GemvProblem p = {packed, x, y, out, in};
+    return x_f16 ? launch_mfma_x<_Float16>(&p, 1, n, ws, stream, max_val, max_idx)
+                 : launch_mfma_x<float>(&p, 1, n, ws, stream, max_val, max_idx);
 }
 
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y, int64_t n,

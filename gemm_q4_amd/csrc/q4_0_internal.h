@@ -53,6 +53,12 @@ hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float 
                             hipStream_t stream);
 hipError_t launch_gemv_mfma_group(const GemvProblem *probs, int count, int64_t n, int x_f16,
                                   void *ws, hipStream_t stream);
+// y (which may be null: not stored) and, per row t of y, its largest value
+// and that value's smallest index, computed in the product's epilogue.
+size_t gemv_mfma_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in);
+hipError_t launch_gemv_mfma_argmax(const void *packed, const void *x, int x_f16, float *y,
+                                   int64_t n, int64_t out, int64_t in, float *max_val,
+                                   int32_t *max_idx, void *ws, hipStream_t stream);
 
 // Prefill kernel: binary16 MFMA on d * (q - 8) rounded to binary16.  When the
 // tiles cannot fill the device it splits K and needs the workspace.

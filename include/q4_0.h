@@ -155,6 +155,24 @@ typedef struct q4_0_linear {
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream);
 
+/* Logit-head product with its epilogue fused: y = x . W^T as in
+ * q4_0_matmul (small-n kernel, n <= 8), and for every row t of y its largest
+ * value max_val[t] and that value's index max_idx[t] (the smallest index
+ * among equal values; NaN never wins; index -1 and a NaN value if no output
+ * of the row is a number).  The output head is the largest matrix of a
+ * decoder and is read once per pass for every state being scored (golem
+ * README, continuous batching: "Several conversations, one pass"); here the
+ * greedy pick is taken while the outputs are still on chip, so a caller that
+ * only needs the pick can pass y = NULL and no n x out array is written.
+ *   y       : [n x out] float32 or NULL.
+ *   max_val : n floats, max_idx : n int32, 4-byte aligned, overlapping
+ *             nothing else.
+ * Returns Q4_0_EUNSUPPORTED for n > 8 or shapes the small-n kernel cannot
+ * take.  max_val[t] is bit-identical to y[t][max_idx[t]] of the same call. */
+int q4_0_matmul_argmax(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
+                       int64_t out, int64_t in, float *max_val, int32_t *max_idx,
+                       void *stream);
+
 /* The kernel q4_0_matmul would run for this call shape (a Q4_0_KERNEL_*
  * value), or a negative status for an invalid shape.  Host only. */
 int q4_0_select_kernel(int64_t n, int64_t out, int64_t in, int x_dtype);

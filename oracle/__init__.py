@@ -129,3 +129,37 @@ def max_ratio(y: np.ndarray, y_ref: np.ndarray, den: np.ndarray) -> float:
     if not np.any(~zero):
         return 0.0
     return float(np.max(err[~zero] / den[~zero]))
+
+
+def greedy_pick(y_ref: np.ndarray):
+    """The greedy pick of a logit head (golem README, "Several conversations,
+    one pass": the output head scores every state of a pass): per row t of
+    y_ref, the largest value and its index, the smallest index among equal
+    values.  A plain scan, written out so ties and NaN are explicit: a NaN
+    never wins; a row with no number gives (nan, -1)."""
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    vals, idxs = [], []
+    for row in y_ref:
+        best, bi = -np.inf, -1
+        for i, v in enumerate(row.tolist()):
+            if v > best or (v == best and bi < 0):
+                best, bi = v, i
+        vals.append(best if bi >= 0 else np.nan)
+        idxs.append(bi)
+    return np.array(vals, dtype=np.float64), np.array(idxs, dtype=np.int64)
+
+
+def pick_within_tolerance(y_ref: np.ndarray, den: np.ndarray, idx: np.ndarray,
+                          tol: float) -> bool:
+    """Whether idx[t] is a correct pick for every row t given outputs that may
+    each be off by up to tol * den: y_ref[t, idx] is within the two outputs'
+    error budgets of the row's true maximum (several indices can be correct
+    when logits nearly tie)."""
+    best, bi = greedy_pick(y_ref)
+    for t, i in enumerate(np.asarray(idx).tolist()):
+        if i < 0 or i >= y_ref.shape[1]:
+            return False
+        slack = tol * (den[t, i] + den[t, bi[t]])
+        if y_ref[t, i] < best[t] - slack:
+            return False
+    return True

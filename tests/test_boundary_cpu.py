@@ -180,3 +180,19 @@ def test_grouped_validation():
     # one y inside another linear's packed weights
     other = (C16 - 16, B16, C16 + (1 << 20), 10, 64)
     assert status_of(grp, [lin, other], q4.F32, 1) == q4.EALIAS
+
+
+def test_argmax_validation():
+    am = q4.q4_0_matmul_argmax
+    D16 = 1 << 38
+    E16 = 1 << 39
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 48, D16, E16, 0) == q4.ESHAPE
+    assert status_of(am, A16, B16, 5, C16, 1, 10, 64, D16, E16, 0) == q4.EINVAL
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, 0, E16, 0) == q4.ENULL
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, D16, 0, 0) == q4.ENULL
+    assert status_of(am, 0, B16, q4.F32, C16, 1, 10, 64, D16, E16, 0) == q4.ENULL
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, D16 + 2, E16, 0) == q4.EALIGN
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, B16 + 4, E16, 0) == q4.EALIAS
+    assert status_of(am, A16, B16, q4.F32, C16, 2, 10, 64, D16, D16 + 4, 0) == q4.EALIAS
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, C16 + 8, E16, 0) == q4.EALIAS
+    assert status_of(am, A16, B16, q4.F32, C16, 9, 10, 64, D16, E16, 0) == q4.EUNSUPPORTED

@@ -364,3 +364,68 @@ def test_graph_replay_matches_eager(kernel, n, out, in_, xdt):
         torch.cuda.synchronize()
         assert torch.equal(y, ref), rep
         assert torch.equal(other, ref)
+
+
+# ------------------------------------------------------------- fused argmax
+def _check_pick(y, mv, mi, blk, x, out, in_, rows_ref=True):
+    """mv/mi against the kernel's own y (bitwise) and against the oracle."""
+    for t in range(y.shape[0]):
+        m = y[t].max()
+        assert mv[t] == m and mi[t] == int(np.flatnonzero(y[t] == m)[0]), t
+    if rows_ref:
+        y_ref, den = oracle.matmul(blk, x, out, in_)
+        assert oracle.pick_within_tolerance(y_ref, den, mi, TOL_SMALL_N)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_argmax_logit_head_full(n):
+    out, in_ = 151936, 2560
+    blk = synth.make_blocks(out, in_, seed=0)
+    x = synth.make_x(n, in_, seed=11)
+    p = packed_from_blocks(blk, out, in_)
+    xd = to_dev(x)
+    y = torch.empty((n, out), device=DEV)
+    mv, mi = q4.matmul_argmax(p, xd, out, y=y)
+    mv2, mi2 = q4.matmul_argmax(p, xd, out)            # no y written
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    _check_pick(yy, mv.cpu().numpy(), mi.cpu().numpy(), blk, x, out, in_)
+    assert np.array_equal(mv.cpu().numpy(), mv2.cpu().numpy())
+    assert np.array_equal(mi.cpu().numpy(), mi2.cpu().numpy())
+    assert np.array_equal(yy, run(p, x, out))          # y equals q4_0_matmul's
+
+
+@pytest.mark.parametrize("n,out,in_", [(8, 2560, 9728),    # K split: pick in the reduction
+                                       (3, 37, 4128), (1, 300, 160), (5, 1, 64)])
+def test_argmax_shapes(n, out, in_):
+    blk = synth.make_blocks(out, in_, seed=21)
+    x = synth.make_x(n, in_, seed=22)
+    p = packed_from_blocks(blk, out, in_)
+    y = torch.empty((n, out), device=DEV)
+    mv, mi = q4.matmul_argmax(p, to_dev(x), out, y=y)
+    torch.cuda.synchronize()
+    _check_pick(y.cpu().numpy(), mv.cpu().numpy(), mi.cpu().numpy(), blk, x, out, in_)
+
+
+def test_argmax_ties_take_the_smallest_index_and_nan_rows_give_minus_one():
+    out, in_ = 300, 128
+    blk = synth.constant_blocks(out, in_, 0x3C00, 0x99)    # every row: d = 1, q = 9
+    x = synth.make_x(3, in_, seed=4)
+    x[1, 5] = np.nan                                        # row 1: every output NaN
+    p = packed_from_blocks(blk, out, in_)
+    mv, mi = q4.matmul_argmax(p, to_dev(x), out)
+    torch.cuda.synchronize()
+    mv, mi = mv.cpu().numpy(), mi.cpu().numpy()
+    assert mi.tolist() == [0, -1, 0]
+    assert np.isnan(mv[1])
+    ref = x.astype(np.float64).sum(axis=1)
+    for t in (0, 2):
+        assert abs(mv[t] - ref[t]) <= TOL_SMALL_N * np.abs(x[t]).sum()
+
+
+def test_argmax_rejects_n_above_8():
+    p = torch.zeros(q4.q4_0_packed_bytes(16, 64), dtype=torch.uint8, device=DEV)
+    x = torch.zeros((9, 64), device=DEV)
+    with pytest.raises(q4.Q4Error) as e:
+        q4.matmul_argmax(p, x, 16)
+    assert e.value.status == q4.EUNSUPPORTED

@@ -318,3 +318,29 @@ def test_brute_force_detects_nibble_order_swap():
     sw[..., 2:] = ((blk[..., 2:] & 0x0F) << 4) | (blk[..., 2:] >> 4)
     yb, _ = brute_force(sw, x)
     assert ya != yb
+
+
+def test_greedy_pick_brute_force_ties_and_nan():
+    """The pick: largest value, smallest index among ties, NaN never wins."""
+    y = np.array([[1.0, 3.0, 3.0, -2.0],
+                  [np.nan, -1.0, -1.0, -5.0],
+                  [np.nan, np.nan, np.nan, np.nan],
+                  [-np.inf, -np.inf, -7.0, -np.inf]])
+    v, i = oracle.greedy_pick(y)
+    assert i.tolist() == [1, 1, -1, 2]
+    assert v[0] == 3.0 and v[1] == -1.0 and np.isnan(v[2]) and v[3] == -7.0
+    rng = np.random.default_rng(5)
+    z = rng.integers(-3, 4, size=(20, 9)).astype(np.float64)
+    v, i = oracle.greedy_pick(z)
+    for t in range(z.shape[0]):
+        m = max(z[t])
+        assert v[t] == m and i[t] == min(k for k in range(9) if z[t, k] == m)
+
+
+def test_pick_within_tolerance_accepts_near_ties_only():
+    y = np.array([[1.0, 1.0 - 1e-9, 0.5]])
+    den = np.full_like(y, 10.0)
+    assert oracle.pick_within_tolerance(y, den, np.array([0]), 1e-3)
+    assert oracle.pick_within_tolerance(y, den, np.array([1]), 1e-3)   # within budget
+    assert not oracle.pick_within_tolerance(y, den, np.array([2]), 1e-3)
+    assert not oracle.pick_within_tolerance(y, den, np.array([-1]), 1e-3)
