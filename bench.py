@@ -351,6 +351,16 @@ def main():
                     extra["decode"].append(decode_line(torch, q4, synth, "logit_head",
                                                        [(151936, 2560)], nn, kernel, 200, 20,
                                                        argmax=True))
+            # the band between decode and prefill: the small-n kernel (16-row
+            # launches) against the tiled prefill product on the same shapes
+            extra["mid_n"] = []
+            up = [(9728, 2560)]
+            for nn in (16, 32):
+                for kk in (q4.KERNEL_AUTO, q4.KERNEL_GEMM):
+                    extra["mid_n"].append(decode_line(torch, q4, synth, "ffn_up_decode", up, nn,
+                                                      kk, 300, 20))
+                extra["mid_n"].append(decode_line(torch, q4, synth, "block_decode", blk, nn,
+                                                  q4.KERNEL_AUTO, 200, 20, groups=bgroups))
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
 
     if args.calib_copy:

@@ -62,11 +62,16 @@ bool supports(int kernel, int64_t n, int64_t out, int64_t in, int x_f16) {
 // Measured on MI355X for n <= 8 over the decode shapes (1024..151936 rows,
 // 1024..9728 columns): the MFMA kernel is as fast as or faster than the VALU
 // kernel everywhere, so it is first; the VALU kernel takes what it cannot.
+// Between decode and prefill (golem README, "Reading a prompt on the card":
+// mat-vec up to 16 columns, tiled products from 32): FFN-up 9728 x 2560 at
+// n = 9..16 runs in 11.1-11.7 us on the small-n kernel against 26.7-29.6 us
+// on the tiled product, and 16-row slices stay ahead up to n = 32 (23 us
+// against 32 us); at n = 48 the tiled product is ahead (33 us against 35).
+constexpr int64_t kSmallNMax = 32;
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
-    if (n <= 8) {
-        if (q4::gemv_mfma_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_MFMA;
-        if (q4::gemv_dpp_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_DPP;
-    }
+    if (n <= kSmallNMax && q4::gemv_mfma_supports(n, out, in, x_f16))
+        return Q4_0_KERNEL_GEMV_MFMA;
+    if (n <= 8 && q4::gemv_dpp_supports(n, out, in, x_f16)) return Q4_0_KERNEL_GEMV_DPP;
     return Q4_0_KERNEL_GEMM;
 }
 
@@ -244,7 +249,18 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
         const int wst = get_workspace(s, &ws);
         if (wst != Q4_0_OK) return wst;
     }
-    return map_hip(q4::launch_gemv_mfma_group(probs, count, n, x_f16, ws, s));
+    // one launch per slice of up to kGemvLaunchRows rows of every x and y
+    const int64_t esize = elem_bytes(x_dtype);
+    for (int64_t r0 = 0; r0 < n; r0 += q4::kGemvLaunchRows) {
+        const int64_t nr = n - r0 < q4::kGemvLaunchRows ? n - r0 : q4::kGemvLaunchRows;
+        q4::GemvProblem ps[Q4_0_MAX_GROUP];
+        for (int i = 0; i < count; ++i)
+            ps[i] = {probs[i].packed, (const uint8_t *)probs[i].x + r0 * probs[i].in * esize,
+                     probs[i].y + r0 * probs[i].out, probs[i].out, probs[i].in};
+        const int st = map_hip(q4::launch_gemv_mfma_group(ps, count, nr, x_f16, ws, s));
+        if (st != Q4_0_OK) return st;
+    }
+    return Q4_0_OK;
 }
 
 const char *q4_0_strerror(int status) {

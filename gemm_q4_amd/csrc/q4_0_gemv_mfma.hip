@@ -1,4 +1,4 @@
-// Small-n Q4_0 product on the matrix cores: y[n x out] = x . W^T for n <= 8,
+// Small-n Q4_0 product on the matrix cores: y[n x out] = x . W^T for n <= 16,
 // for one linear or for a group of linears that share n in one launch.
 //
 // Why MFMA for a memory-bound product: a vector-ALU dot costs about n + 1.25
@@ -23,6 +23,9 @@
 //   D: lane l holds slots 4*(l/16)+i, i = 0..3, of weight row l%16; per block
 //      acc += d * D in float32 (d is the row's binary16 scale).
 // hi and lo slots of a row are summed with one cross-lane shuffle (xor 32).
+// From 9 to 16 rows (the band between decode and prefill) each row takes one
+// slot holding its scaled binary16 value, without a low part: the precision
+// of the prefill kernel, which rounds x to binary16 as well (2^-11 relative).
 //
 // Work split.  A workgroup owns a run of 16-row tiles of one linear and one
 // of its S slices of K; its waves take contiguous runs of `per` <= GPW
@@ -62,6 +65,12 @@ namespace q4 {
 #define Q4_MFMA_GROUPS_PER_WAVE 5
 #endif
 constexpr int kMfmaMaxWaves = 8;
+constexpr int kMaxRows = (int)kGemvLaunchRows;   // activation rows of one launch
+// rows <= 8: high and low binary16 part of each row (2n slots); 9..16 rows:
+// one binary16 slot per row
+template <int NT> constexpr bool split_rows() { return NT <= 8; }
+template <int NT> constexpr int row_slots() { return NT <= 8 ? 2 * NT : NT; }
+static int64_t slots_for(int64_t n) { return n <= 8 ? 2 * n : n; }
 constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
 // x items (8 values each) a lane holds while it stages: caps groups per wave x n
@@ -206,9 +215,10 @@ __device__ void amax_workgroup(float (&bv)[NT], int (&bi)[NT], uint2 *out) {
 // converts row t: item (block b, quarter g) holds the 8 values k = 32b + 4g +
 // {0..3, 16..19}; each thread loads its items (kPrepItems of them in
 // registers, more in further passes that load again), the workgroup finds
-// the row's largest |x|, and each item is written as slot j in [0, 2*NT)
-// (j < NT: high part of row j; j >= NT: low part of row j - NT) and quarter
-// g, 16 bytes at kFragHeader + ((b * 2*NT + j) * 4 + g) * 16.  Blocks past in
+// the row's largest |x|, and each item is written as slot j in [0, S)
+// (S = 2*NT for NT <= 8: j < NT high part of row j, j >= NT low part of row
+// j - NT; S = NT above 8 rows: row j) and quarter g, 16 bytes at
+// kFragHeader + ((b * S + j) * 4 + g) * 16.  Blocks past in
 // (up to the padded group) are zeros.  Float at byte 4t: the inverse of row
 // t's scale.  One memory round trip for rows up to 512 * kPrepItems / 4
 // blocks.
@@ -259,12 +269,14 @@ __global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restric
     const float sc = row_scale(m);
     if (threadIdx.x == 0) reinterpret_cast<float *>(frag)[t] = inverse_pow2(sc);
     uint8_t *f = frag + kFragHeader;
+    constexpr int kS = row_slots<NT>();
     auto store = [&](int it, const float w[8]) {
         const int b = it >> 2, gq = it & 3;
         h8_t fh, fl;
         split_fragment(w, sc, fh, fl);
-        *reinterpret_cast<h8_t *>(f + ((b * 2 * NT + t) * 4 + gq) * 16) = fh;
-        *reinterpret_cast<h8_t *>(f + ((b * 2 * NT + NT + t) * 4 + gq) * 16) = fl;
+        *reinterpret_cast<h8_t *>(f + ((b * kS + t) * 4 + gq) * 16) = fh;
+        if constexpr (split_rows<NT>())
+            *reinterpret_cast<h8_t *>(f + ((b * kS + NT + t) * 4 + gq) * 16) = fl;
     };
 #pragma unroll
     for (int i = 0; i < kPrepItems; ++i) {
@@ -320,11 +332,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     }
 
     // lane's A slot r: high part of row r (r < NT), low part of row r - 8
-    // (8 <= r < 8 + NT).  Lanes of unused slots read slot 0's fragment: a D
-    // row depends only on its own A row, and the rows of unused slots are
-    // never read, so their contents do not matter (they stay finite).
-    const int jslot = r < NT ? r : ((r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
-    constexpr int kBlockFrag = 2 * NT * 64;                   // fragment bytes per block
+    // (8 <= r < 8 + NT); above 8 rows, row r.  Lanes of unused slots read
+    // slot 0's fragment: a D row depends only on its own A row, and the rows
+    // of unused slots are never read, so their contents do not matter (they
+    // stay finite).
+    constexpr bool kSplit = split_rows<NT>();
+    const int jslot = r < NT ? r : ((kSplit && r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
+    constexpr int kBlockFrag = row_slots<NT>() * 64;          // fragment bytes per block
     const int gw = ng > 0 ? gs0 + q0 : gs0;                   // first group of the wave
 
     // ---- prepared launch: request this lane's fragments ------------------------
@@ -423,8 +437,10 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             for (int tt = 1; tt < NT; ++tt) sc = t == tt ? scale[tt] : sc;
             h8_t fh, fl;
             split_fragment(xv[ii], sc, fh, fl);
-            *reinterpret_cast<h8_t *>(frag + ((bl * 2 * NT + t) * 4 + gq) * 16) = fh;
-            *reinterpret_cast<h8_t *>(frag + ((bl * 2 * NT + NT + t) * 4 + gq) * 16) = fl;
+            constexpr int kS = row_slots<NT>();
+            *reinterpret_cast<h8_t *>(frag + ((bl * kS + t) * 4 + gq) * 16) = fh;
+            if constexpr (kSplit)
+                *reinterpret_cast<h8_t *>(frag + ((bl * kS + NT + t) * 4 + gq) * 16) = fl;
         }
     }
     // the fragments are read back by other lanes of this wave only: LDS
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     float inv[kLive];
 #pragma unroll
     for (int i = 0; i < kLive; ++i) {
-        const int row = (4 * g + i) & 7;
+        const int row = kSplit ? ((4 * g + i) & 7) : 4 * g + i;
         if constexpr (PREP) {
             inv[i] = row < NT ? reinterpret_cast<const float *>(a.frag)[row] : 1.0f;
         } else {
@@ -493,9 +509,9 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
 #pragma unroll
         for (int i = 0; i < kLive; ++i) {
             v[i] = acc[i] * inv[i];
-            v[i] += __shfl_xor(v[i], 32);
+            if constexpr (kSplit) v[i] += __shfl_xor(v[i], 32);
         }
-        if (g < 2) {
+        if (!kSplit || g < 2) {
 #pragma unroll
             for (int i = 0; i < kLive; ++i)
                 if (4 * g + i < NT) red[slot][wave][4 * g + i][r] = v[i];
@@ -521,7 +537,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                         if (u == tt) amax_update(sum, row, bv[u], bi[u]);
                 }
             } else {
-                a.part[(((int64_t)sy * a.tiles + t) * 8 + tt) * 16 + rr] = sum;
+                a.part[(((int64_t)sy * a.tiles + t) * kMaxRows + tt) * 16 + rr] = sum;
             }
         }
         __syncthreads();
@@ -581,7 +597,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
         const int64_t t = (e >> 4) / NT;
         float s = 0.0f;
         for (int64_t q = 0; q < L.slices; ++q)
-            s += L.part[((q * L.tiles + t) * 8 + tt) * 16 + rr];
+            s += L.part[((q * L.tiles + t) * kMaxRows + tt) * 16 + rr];
         const int64_t row = t * kTileRows + rr;
         if (row < L.out) {
             if (L.y) L.y[(int64_t)tt * L.out + row] = s;
@@ -624,14 +640,16 @@ __global__ __launch_bounds__(256) void amax_final_kernel(const uint2 *__restrict
     }
 }
 
-static int64_t mfma_lds_bytes(int64_t n, int64_t groups) { return groups * 4 * 2 * n * 64; }
+static int64_t mfma_lds_bytes(int64_t n, int64_t groups) {
+    return groups * 4 * slots_for(n) * 64;
+}
 
 static int64_t round256(int64_t b) { return (b + 255) & ~(int64_t)255; }
 
 // Bytes of the prepared fragments of an [n x in] x (header included).
 static int64_t frag_bytes(int64_t n, int64_t in) {
     const Layout L(1, in);
-    return round256(kFragHeader + L.g4 * 4 * 2 * n * 64);
+    return round256(kFragHeader + L.g4 * 4 * slots_for(n) * 64);
 }
 
 // Whether launches with n rows of x of width `in` use the pre-pass.
@@ -653,7 +671,7 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     // prepared, the A fragments of its range
     int64_t per_cap = prep ? kPrepMaxGroups : (kMaxStageItems * 64) / (16 * n);
     if (per_cap > 16) per_cap = 16;
-    if (per_cap < 1) per_cap = 1;     // n > 8: no plan can run (gemv_mfma_supports)
+    if (per_cap < 1) per_cap = 1;     // n > 16: no plan can run (gemv_mfma_supports)
     // slices: as few as keep the slice within the waves' capacity and, when
     // x is staged in LDS, its A fragments within the LDS budget
     int64_t gps_max = per_cap * kMfmaMaxWaves;
@@ -684,7 +702,7 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
 static size_t mfma_part_bytes(const MfmaPlan &p, int64_t out, int64_t in) {
     if (p.slices == 1) return 0;
     const Layout L(out, in);
-    return (size_t)round256(p.slices * L.tiles * 8 * 16 * (int64_t)sizeof(float));
+    return (size_t)round256(p.slices * L.tiles * kMaxRows * 16 * (int64_t)sizeof(float));
 }
 
 // (max, index) pairs of an argmax launch: one per row per workgroup of the
@@ -695,25 +713,54 @@ static int64_t amax_pairs(const MfmaPlan &p, int64_t n, int64_t out, int64_t in)
     return wgs * n;
 }
 
-size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in) {
+// Launches above kMaxRows rows run as consecutive launches of up to
+// kMaxRows rows each (the row slices of x and y), which read the weights
+// once per slice; up to kMaxSlicedRows rows.
+constexpr int64_t kMaxSlicedRows = 64;
+
+static size_t launch_workspace_bytes(int64_t n, int64_t out, int64_t in) {
     const size_t part = mfma_part_bytes(mfma_plan(n, out, in), out, in);
     return part + (use_prep(n, in) ? (size_t)frag_bytes(n, in) : 0);
 }
 
-size_t gemv_mfma_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
+static size_t launch_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
     const MfmaPlan p = mfma_plan(n, out, in);
-    return gemv_mfma_workspace_bytes(n, out, in) +
+    return launch_workspace_bytes(n, out, in) +
            (size_t)round256(amax_pairs(p, n, out, in) * (int64_t)sizeof(uint2));
 }
 
-bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
-    (void)x_f16;
-    if (n < 1 || n > 8) return false;
+static bool launch_supported(int64_t n, int64_t out, int64_t in) {
+    if (n < 1 || n > kMaxRows) return false;
     const MfmaPlan p = mfma_plan(n, out, in);
     if (p.gpw == 0 || p.waves > kMfmaMaxWaves || p.slices > 65535) return false;
     if ((int64_t)p.waves * p.per < p.gps) return false;
     if (p.gx * p.slices > 0x7fffffff) return false;
-    return gemv_mfma_workspace_bytes(n, out, in) <= kWorkspaceBytes;
+    return launch_workspace_bytes(n, out, in) <= kWorkspaceBytes;
+}
+
+// The row counts of the slices of an n-row call: full kMaxRows slices and
+// the remainder (each slice's needs are those of its row count).
+static int64_t tail_rows(int64_t n) { return n % kMaxRows == 0 ? kMaxRows : n % kMaxRows; }
+
+size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in) {
+    if (n <= kMaxRows) return launch_workspace_bytes(n, out, in);
+    const size_t a = launch_workspace_bytes(kMaxRows, out, in);
+    const size_t b = launch_workspace_bytes(tail_rows(n), out, in);
+    return a > b ? a : b;
+}
+
+size_t gemv_mfma_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
+    if (n <= kMaxRows) return launch_argmax_workspace_bytes(n, out, in);
+    const size_t a = launch_argmax_workspace_bytes(kMaxRows, out, in);
+    const size_t b = launch_argmax_workspace_bytes(tail_rows(n), out, in);
+    return a > b ? a : b;
+}
+
+bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
+    (void)x_f16;
+    if (n < 1 || n > kMaxSlicedRows) return false;
+    if (n <= kMaxRows) return launch_supported(n, out, in);
+    return launch_supported(kMaxRows, out, in) && launch_supported(tail_rows(n), out, in);
 }
 
 int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in) {
@@ -861,6 +908,14 @@ static hipError_t launch_mfma_x(const GemvProblem *probs, int count, int64_t n, 
     case 6: return launch_mfma_t<6, XT>(probs, count, ws, stream, mv, mi);
     case 7: return launch_mfma_t<7, XT>(probs, count, ws, stream, mv, mi);
     case 8: return launch_mfma_t<8, XT>(probs, count, ws, stream, mv, mi);
+    case 9: return launch_mfma_t<9, XT>(probs, count, ws, stream, mv, mi);
+    case 10: return launch_mfma_t<10, XT>(probs, count, ws, stream, mv, mi);
+    case 11: return launch_mfma_t<11, XT>(probs, count, ws, stream, mv, mi);
+    case 12: return launch_mfma_t<12, XT>(probs, count, ws, stream, mv, mi);
+    case 13: return launch_mfma_t<13, XT>(probs, count, ws, stream, mv, mi);
+    case 14: return launch_mfma_t<14, XT>(probs, count, ws, stream, mv, mi);
+    case 15: return launch_mfma_t<15, XT>(probs, count, ws, stream, mv, mi);
+    case 16: return launch_mfma_t<16, XT>(probs, count, ws, stream, mv, mi);
     default: return hipErrorInvalidValue;
     }
 }
@@ -875,15 +930,30 @@ hipError_t launch_gemv_mfma_group(const GemvProblem *probs, int count, int64_t n
 hipError_t launch_gemv_mfma_argmax(const void *packed, const void *x, int x_f16, float *y,
                                    int64_t n, int64_t out, int64_t in, float *max_val,
                                    int32_t *max_idx, void *ws, hipStream_t stream) {
-    const GemvProblem p = {packed, x, y, out, in};
-    return x_f16 ? launch_mfma_x<_Float16>(&p, 1, n, ws, stream, max_val, max_idx)
-                 : launch_mfma_x<float>(&p, 1, n, ws, stream, max_val, max_idx);
+    const int64_t esize = x_f16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < n; r0 += kMaxRows) {
+        const int64_t nr = n - r0 < kMaxRows ? n - r0 : kMaxRows;
+        const GemvProblem p = {packed, (const uint8_t *)x + r0 * in * esize,
+                               y ? y + r0 * out : nullptr, out, in};
+        const hipError_t e =
+            x_f16 ? launch_mfma_x<_Float16>(&p, 1, nr, ws, stream, max_val + r0, max_idx + r0)
+                  : launch_mfma_x<float>(&p, 1, nr, ws, stream, max_val + r0, max_idx + r0);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y, int64_t n,
                             int64_t out, int64_t in, void *ws, hipStream_t stream) {
-    const GemvProblem p = {packed, x, y, out, in};
-    return launch_gemv_mfma_group(&p, 1, n, x_f16, ws, stream);
+    const int64_t esize = x_f16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < n; r0 += kMaxRows) {
+        const int64_t nr = n - r0 < kMaxRows ? n - r0 : kMaxRows;
+        const GemvProblem p = {packed, (const uint8_t *)x + r0 * in * esize, y + r0 * out, out,
+                               in};
+        const hipError_t e = launch_gemv_mfma_group(&p, 1, nr, x_f16, ws, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q4

@@ -62,8 +62,10 @@ extern "C" {
 #define Q4_0_KERNEL_AUTO 0      /* what q4_0_matmul runs                      */
 #define Q4_0_KERNEL_GEMV_DPP 1  /* small n: VALU dot, x in LDS, DPP/shuffle
                                    reduction; n <= 8                          */
-#define Q4_0_KERNEL_GEMV_MFMA 2 /* small n: fp16 MFMA on split activations;
-                                   n <= 8                                     */
+#define Q4_0_KERNEL_GEMV_MFMA 2 /* small n: fp16 MFMA; n <= 8: activations
+                                   split into high and low binary16 parts;
+                                   9..16: one binary16 part; 17..64: 16-row
+                                   slices, one launch each                    */
 #define Q4_0_KERNEL_GEMM 3      /* prefill: tiles dequantized to fp16, MFMA   */
 
 /* Largest sizes accepted (32-bit grid and index limits). */
@@ -115,8 +117,9 @@ int q4_0_unpack(const void *packed, void *blocks, int64_t out, int64_t in,
  *   n, out, in : 1 <= n <= Q4_0_MAX_N, 1 <= out <= Q4_0_MAX_OUT,
  *            32 <= in <= Q4_0_MAX_IN, in % 32 == 0.
  * Accuracy, as max |y - y_exact| / sum_k |w x| over outputs: <= 1e-3 on the
- * small-n kernels (float32 accumulation), <= 1e-2 on the prefill kernel
- * (binary16 operands; float32 activations are rounded to binary16 there). */
+ * small-n kernels for n <= 8 (float32 accumulation, 22-bit activations),
+ * <= 1e-2 where activations are rounded to binary16: the small-n MFMA kernel
+ * above 8 rows and the prefill kernel (which also rounds the weights). */
 int q4_0_matmul(const void *packed, const void *x, int x_dtype, float *y,
                 int64_t n, int64_t out, int64_t in, void *stream);
 
@@ -148,10 +151,11 @@ typedef struct q4_0_linear {
  *             each is checked as q4_0_matmul checks its arguments.
  *   No y may overlap any x, any packed W or another y of the group
  *   (Q4_0_EALIAS).  The x of different linears may be the same buffer.
- * When the small-n MFMA kernel takes every linear (n <= 8) the group runs as
- * one launch (plus one reduction launch if a linear splits K); otherwise
- * each linear runs as q4_0_matmul would, in array order.  Results equal those
- * of q4_0_matmul on each linear alone, bit for bit. */
+ * When q4_0_matmul would run the small-n MFMA kernel on every linear
+ * (n <= 32 for the usual shapes) the group runs as one launch per 16 rows
+ * (plus the activation pre-pass from 4 rows, and a reduction launch if a
+ * linear splits K); otherwise each linear runs as q4_0_matmul would, in array
+ * order.  Results equal those of q4_0_matmul on each linear alone. */
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream);
 
@@ -167,8 +171,9 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
  *   y       : [n x out] float32 or NULL.
  *   max_val : n floats, max_idx : n int32, 4-byte aligned, overlapping
  *             nothing else.
- * Returns Q4_0_EUNSUPPORTED for n > 8 or shapes the small-n kernel cannot
- * take.  max_val[t] is bit-identical to y[t][max_idx[t]] of the same call. */
+ * Returns Q4_0_EUNSUPPORTED for shapes the small-n MFMA kernel cannot take
+ * (n > 64 among them).  max_val[t] is bit-identical to y[t][max_idx[t]] of
+ * the same call. */
 int q4_0_matmul_argmax(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
                        int64_t out, int64_t in, float *max_val, int32_t *max_idx,
                        void *stream);

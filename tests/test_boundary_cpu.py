@@ -107,10 +107,10 @@ def test_matmul_validation(args, expect):
 def test_matmul_ex_rejects_bad_kernel_and_unsupported_shapes():
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, 9, 0) == q4.EINVAL
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, -1, 0) == q4.EINVAL
-    # small-n kernels take n <= 8 only
+    # the VALU kernel takes n <= 8, the small-n MFMA kernel n <= 64
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 9, 10, 64,
                      q4.KERNEL_GEMV_DPP, 0) == q4.EUNSUPPORTED
-    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 9, 10, 64,
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 65, 10, 64,
                      q4.KERNEL_GEMV_MFMA, 0) == q4.EUNSUPPORTED
     # the LDS-staged kernel cannot hold 8 rows of a 16384-wide x
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 8, 10, 16384,
@@ -137,7 +137,10 @@ def test_kernel_choice_table():
             assert sel(n, out, in_) in (q4.KERNEL_GEMV_DPP, q4.KERNEL_GEMV_MFMA)
     assert sel(512, 9728, 2560, q4.F16) == q4.KERNEL_GEMM
     assert sel(512, 2560, 9728, q4.F16) == q4.KERNEL_GEMM
-    assert sel(9, 100, 64) == q4.KERNEL_GEMM
+    # the band between decode and prefill: small-n MFMA kernel up to 32 rows
+    assert sel(9, 100, 64) == q4.KERNEL_GEMV_MFMA
+    assert sel(32, 9728, 2560) == q4.KERNEL_GEMV_MFMA
+    assert sel(33, 9728, 2560) == q4.KERNEL_GEMM
     with pytest.raises(q4.Q4Error):
         sel(0, 10, 64)
     with pytest.raises(q4.Q4Error):
@@ -147,7 +150,9 @@ def test_kernel_choice_table():
 def test_kernel_supports():
     assert q4.q4_0_kernel_supports(q4.KERNEL_GEMM, 512, 9728, 2560, q4.F16)
     assert q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 8, 2560, 9728)
-    assert not q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 9, 2560, 9728)
+    assert q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 16, 2560, 9728)
+    assert q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 64, 151936, 2560)
+    assert not q4.q4_0_kernel_supports(q4.KERNEL_GEMV_MFMA, 65, 2560, 9728)
     with pytest.raises(q4.Q4Error):
         q4.q4_0_kernel_supports(17, 1, 10, 64)
 
@@ -195,4 +200,4 @@ def test_argmax_validation():
     assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, B16 + 4, E16, 0) == q4.EALIAS
     assert status_of(am, A16, B16, q4.F32, C16, 2, 10, 64, D16, D16 + 4, 0) == q4.EALIAS
     assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, C16 + 8, E16, 0) == q4.EALIAS
-    assert status_of(am, A16, B16, q4.F32, C16, 9, 10, 64, D16, E16, 0) == q4.EUNSUPPORTED
+    assert status_of(am, A16, B16, q4.F32, C16, 65, 10, 64, D16, E16, 0) == q4.EUNSUPPORTED
