@@ -30,6 +30,11 @@ class Oracle:
         lib.q4o_matmul_rows.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64,
                                         vp, i64, vp, vp, ctypes.c_int]
         lib.q4o_matmul_rows.restype = ctypes.c_int
+        lib.q4o_quantize_x8.argtypes = [vp, i64, i64, vp, vp]
+        lib.q4o_quantize_x8.restype = ctypes.c_int
+        lib.q4o_matmul_w4a8_rows.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp,
+                                             ctypes.c_int]
+        lib.q4o_matmul_w4a8_rows.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -82,6 +87,43 @@ class Oracle:
         return (y, den, rc) if return_threads else (y, den)
 
 
+    def quantize_x8(self, x: np.ndarray):
+        """(q int8 [n x in], d float32 [n x in/32]): x quantized per 32-value
+        block (see q4o_quantize_x8)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        n, in_ = x.shape
+        q = np.empty((n, in_), dtype=np.int8)
+        d = np.empty((n, in_ // 32), dtype=np.float32)
+        if self.lib.q4o_quantize_x8(_ptr(x), n, in_, _ptr(q), _ptr(d)) != 0:
+            raise ValueError("oracle rejected the shape")
+        return q, d
+
+    def matmul_w4a8(self, blocks: np.ndarray, q: np.ndarray, d: np.ndarray, out: int,
+                    in_: int, rows=None, nthreads: int = 0):
+        """(y, den) float64 [n x len(rows)] of the W4A8 product on quantized
+        activations (q, d) (see q4o_matmul_w4a8_rows)."""
+        blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        d = np.ascontiguousarray(d, dtype=np.float32)
+        if in_ % 32 or blocks.size != out * (in_ // 32) * 18:
+            raise ValueError("block buffer does not match out x in")
+        n = q.shape[0]
+        if q.shape != (n, in_) or d.shape != (n, in_ // 32):
+            raise ValueError("q must be [n x in] and d [n x in/32]")
+        if rows is None:
+            nrows, rp = out, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            nrows, rp = rows_arr.size, _ptr(rows_arr)
+        y = np.empty((n, nrows), dtype=np.float64)
+        den = np.empty((n, nrows), dtype=np.float64)
+        rc = self.lib.q4o_matmul_w4a8_rows(_ptr(blocks), _ptr(q), _ptr(d), n, out, in_, rp,
+                                          nrows, _ptr(y), _ptr(den), nthreads)
+        if rc < 0:
+            raise ValueError(f"oracle failed with status {rc}")
+        return y, den
+
+
 _DEFAULT = None
 
 
@@ -111,6 +153,14 @@ def dequantize(blocks, out, in_):
 
 def matmul(blocks, x, out, in_, rows=None, nthreads=0, return_threads=False):
     return default().matmul(blocks, x, out, in_, rows, nthreads, return_threads)
+
+
+def quantize_x8(x):
+    return default().quantize_x8(x)
+
+
+def matmul_w4a8(blocks, q, d, out, in_, rows=None, nthreads=0):
+    return default().matmul_w4a8(blocks, q, d, out, in_, rows, nthreads)
 
 
 def max_ratio(y: np.ndarray, y_ref: np.ndarray, den: np.ndarray) -> float:

@@ -209,3 +209,132 @@ int q4o_matmul(const uint8_t *blocks, const void *x, int x_is_f16,
     return q4o_matmul_rows(blocks, x, x_is_f16, n, out, in, NULL, out,
                            y, den, nthreads);
 }
+
+/*
+ * W4A8: int4 weights against int8 activations.
+ *
+ * What it follows: rembed "Architecture", section "int8 quantization" (full
+ * int8: activations quantized to 8-bit integers, an integer dot product per
+ * output, an offset correction subtracted in the epilogue, checked bit for
+ * bit against an integer reference) and the goinfer primer ch. 10 "Which
+ * kernel runs is a runtime decision" (the quantized dot on 8-bit integer
+ * dot-product hardware).  The pages do not give the activations' scale
+ * granularity; the reading taken here is one scale per 32 activations of a
+ * row, the weights' block size, so that every block's integer sum is scaled
+ * once: d = max |x| / 127 over the block (float32 division), q = x / d
+ * rounded to nearest, ties to even (float32 division, then rint), and q = 0
+ * for every value of a block whose d is not a positive finite number.
+ */
+
+/* Quantize x [n x in] (float32) per 32-value block: q [n x in] int8 codes,
+ * d [n x in/32] float32 scales.  Returns 0, or -1 on a bad shape. */
+int q4o_quantize_x8(const float *x, int64_t n, int64_t in, int8_t *q, float *d)
+{
+    if (!x || !q || !d || n <= 0 || in <= 0 || in % Q4O_BLOCK)
+        return -1;
+    int64_t nb = in / Q4O_BLOCK;
+    for (int64_t t = 0; t < n; ++t)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + t * in + b * Q4O_BLOCK;
+            float amax = 0.0f;
+            for (int j = 0; j < Q4O_BLOCK; ++j) {
+                float a = fabsf(xb[j]);
+                if (a > amax || a != a)      /* a NaN makes the maximum NaN */
+                    amax = a;
+            }
+            float s = amax / 127.0f;
+            d[t * nb + b] = s;
+            int ok = s > 0.0f && s <= 3.4028234663852886e38f;
+            for (int j = 0; j < Q4O_BLOCK; ++j)
+                q[t * in + b * Q4O_BLOCK + j] = ok ? (int8_t)rintf(xb[j] / s) : 0;
+        }
+    return 0;
+}
+
+typedef struct {
+    const uint8_t *blocks;
+    const int8_t *q;     /* [n x in] */
+    const float *d;      /* [n x nb] */
+    int64_t n, out, in;
+    const int64_t *rows;
+    int64_t nrows;
+    double *y, *den;
+    int64_t lo, hi;
+} q4o_job8;
+
+static void *q4o_worker8(void *arg)
+{
+    q4o_job8 *j = (q4o_job8 *)arg;
+    int64_t nb = j->in / Q4O_BLOCK;
+    for (int64_t i = j->lo; i < j->hi; ++i) {
+        int64_t o = j->rows ? j->rows[i] : i;
+        for (int64_t t = 0; t < j->n; ++t) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *blk = j->blocks + (o * nb + b) * Q4O_BLOCK_BYTES;
+                double dw = (double)q4o_half_to_float((uint16_t)(blk[0] | (blk[1] << 8)));
+                double dx = (double)j->d[t * nb + b];
+                const int8_t *qx = j->q + t * j->in + b * Q4O_BLOCK;
+                int64_t isum = 0, iabs = 0;
+                for (int k = 0; k < Q4O_BLOCK; ++k) {
+                    int64_t p = (int64_t)(q4o_code(blk + 2, k) - 8) * (int64_t)qx[k];
+                    isum += p;
+                    iabs += p < 0 ? -p : p;
+                }
+                acc += dw * dx * (double)isum;           /* exact product */
+                mag += fabs(dw * dx) * (double)iabs;
+            }
+            j->y[t * j->nrows + i] = acc;
+            if (j->den)
+                j->den[t * j->nrows + i] = mag;
+        }
+    }
+    return NULL;
+}
+
+/* y[t, i] = sum_b dw[o, b] * d[t, b] * sum_{k in b} (qw[o, k] - 8) * q[t, k]
+ * for rows[i] (every row when rows is NULL), with exact integer block sums
+ * and float64 scaling; den[t, i] = sum_b |dw d| * sum_k |(qw - 8) q|.
+ * Returns the number of threads used, or a negative value on error. */
+int q4o_matmul_w4a8_rows(const uint8_t *blocks, const int8_t *q, const float *d,
+                         int64_t n, int64_t out, int64_t in,
+                         const int64_t *rows, int64_t nrows,
+                         double *y, double *den, int nthreads)
+{
+    if (!blocks || !q || !d || !y || n <= 0 || out <= 0 || in <= 0 || in % Q4O_BLOCK)
+        return -1;
+    if (!rows && nrows != out)
+        return -1;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= out)
+            return -1;
+    if (nthreads <= 0)
+        nthreads = q4o_hw_threads();
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    if (nthreads < 1)
+        nthreads = 1;
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    q4o_job8 *jobs = (q4o_job8 *)calloc((size_t)nthreads, sizeof(q4o_job8));
+    if (!tid || !jobs) {
+        free(tid); free(jobs);
+        return -2;
+    }
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        q4o_job8 *j = &jobs[i];
+        j->blocks = blocks; j->q = q; j->d = d; j->n = n; j->out = out; j->in = in;
+        j->rows = rows; j->nrows = nrows; j->y = y; j->den = den;
+        j->lo = nrows * i / nthreads;
+        j->hi = nrows * (i + 1) / nthreads;
+        if (pthread_create(&tid[i], NULL, q4o_worker8, j) != 0) {
+            nthreads = i;
+            rc = -2;
+            break;
+        }
+    }
+    for (int i = 0; i < nthreads; ++i)
+        pthread_join(tid[i], NULL);
+    free(tid); free(jobs);
+    return rc < 0 ? rc : nthreads;
+}

@@ -4,7 +4,9 @@ oracle's C source and compiled on the CPU, fails at least one of them.
 The planted mistakes: the interleaved nibble order instead of split-half, a
 dropped or reversed offset of 8, a big-endian scale, a wrong scale index, a
 dropped last term, transposed activation or output indexing, a wrong
-binary16 exponent bias or subnormal scale, a signed magnitude sum.
+binary16 exponent bias or subnormal scale, a signed magnitude sum; in the
+W4A8 part, ties rounded away from zero, a 255 instead of a 127 scale, a
+signed maximum, a dropped offset, the first block's activation scale.
 """
 import os
 import tempfile
@@ -15,7 +17,7 @@ import pytest
 import oracle
 from oracle import build as obuild
 import synth
-from test_oracle_pins import (GOLDEN_CASES, _golden_blocks, brute_force)
+from test_oracle_pins import (GOLDEN_CASES, _brute_w4a8, _golden_blocks, brute_force)
 
 SRC = open(obuild.SRC).read()
 
@@ -40,6 +42,13 @@ MUTANTS = {
                   "v = ldexpf((float)(1024 + f), e - 24);"),
     "half_subnormal": ("v = ldexpf((float)f, -24);", "v = ldexpf((float)f, -25);"),
     "signed_den": ("mag += fabs(p);", "mag += p;"),
+    "x8_ties_away": ("(int8_t)rintf(xb[j] / s)", "(int8_t)roundf(xb[j] / s)"),
+    "x8_scale_255": ("float s = amax / 127.0f;", "float s = amax / 255.0f;"),
+    "x8_signed_max": ("float a = fabsf(xb[j]);", "float a = xb[j];"),
+    "w4a8_no_offset": ("(int64_t)(q4o_code(blk + 2, k) - 8) * (int64_t)qx[k]",
+                       "(int64_t)(q4o_code(blk + 2, k)) * (int64_t)qx[k]"),
+    "w4a8_first_dx": ("double dx = (double)j->d[t * nb + b];",
+                      "double dx = (double)j->d[t * nb];"),
 }
 
 
@@ -83,6 +92,24 @@ def battery(o):
         if not ok:
             failed.append("brute")
             break
+    # W4A8: hand-worked quantizer block, reconstruction bound, brute force
+    xq = np.array([[127.0, 0.5, 1.5, 2.5, -1.5, -127.0, 63.5, -0.49] + [0.0] * 24 +
+                   [-3.0, 1.0] + [0.0] * 30], np.float32)
+    q, d = o.quantize_x8(xq)
+    if q[0, :8].tolist() != [127, 0, 2, 2, -2, -127, 64, 0] or d[0, 1] != np.float32(3) / 127:
+        failed.append("x8_hand")
+    xr = synth.make_x(2, 128, seed=5)
+    q, d = o.quantize_x8(xr)
+    dd = np.repeat(d.astype(np.float64), 32, axis=1)
+    if not (np.all(np.abs(xr - q * dd) <= dd * (0.5 + 1e-5)) and np.abs(q).max() == 127):
+        failed.append("x8_bound")
+    blk = synth.make_blocks(3, 64, seed=8)
+    q, d = o.quantize_x8(synth.make_x(2, 64, seed=8))
+    y, den = o.matmul_w4a8(blk, q, d, 3, 64)
+    ye, de = _brute_w4a8(blk.reshape(3, 2, 18), q, d)
+    if not all(abs(Fraction(y[t, r]) - ye[t][r]) <= Fraction(1e-12) * de[t][r]
+               for t in range(2) for r in range(3)):
+        failed.append("w4a8_brute")
     return failed
 
 
@@ -93,7 +120,7 @@ def test_unmutated_oracle_passes_battery():
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name):
     old, new = MUTANTS[name]
-    assert SRC.count(old) == 1, f"mutation site for {name} not found"
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
     with tempfile.TemporaryDirectory() as tmp:
         src = os.path.join(tmp, "mut.c")
         with open(src, "w") as f:

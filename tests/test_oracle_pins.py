@@ -344,3 +344,110 @@ def test_pick_within_tolerance_accepts_near_ties_only():
     assert oracle.pick_within_tolerance(y, den, np.array([1]), 1e-3)   # within budget
     assert not oracle.pick_within_tolerance(y, den, np.array([2]), 1e-3)
     assert not oracle.pick_within_tolerance(y, den, np.array([-1]), 1e-3)
+
+
+# ------------------------------------------------------------------- W4A8
+def test_quantize_x8_hand_worked_block():
+    """amax 127 gives d = 1 exactly, so the codes are x rounded to nearest,
+    ties to even; the largest magnitude maps to +-127."""
+    blockv = [127.0, 0.5, 1.5, 2.5, -1.5, -127.0, 63.5, -0.49, 3.0, 126.5] + [0.0] * 22
+    x = np.array([blockv], dtype=np.float32)
+    q, d = oracle.quantize_x8(x)
+    assert d[0, 0] == 1.0
+    assert q[0, :10].tolist() == [127, 0, 2, 2, -2, -127, 64, 0, 3, 126]
+    assert not q[0, 10:].any()
+
+
+def test_quantize_x8_zero_and_nan_blocks():
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[1, 40] = np.nan
+    x[1, 41] = 5.0
+    x[1, 3] = 2.0
+    q, d = oracle.quantize_x8(x)
+    assert d[0].tolist() == [0.0, 0.0] and not q[0].any()
+    assert np.isnan(d[1, 1]) and not q[1, 32:].any()      # NaN block: codes 0
+    assert d[1, 0] == np.float32(2.0) / np.float32(127.0) and q[1, 3] == 127
+
+
+@pytest.mark.parametrize("scale", [1e-30, 1e-3, 1.0, 1e4, 1e30])
+def test_quantize_x8_reconstruction_bound_and_order(scale):
+    """|x - q d| <= d/2 (plus float32 rounding of d), |q| <= 127 with the
+    block's largest magnitude at +-127, and codes ordered as the values."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((5, 256)) * scale).astype(np.float32)
+    q, d = oracle.quantize_x8(x)
+    xb = x.reshape(5, 8, 32).astype(np.float64)
+    qb = q.reshape(5, 8, 32).astype(np.float64)
+    dd = d.astype(np.float64)[..., None]
+    assert np.all(np.abs(qb) <= 127)
+    assert np.all(np.abs(xb - qb * dd) <= dd * (0.5 + 1e-5))
+    top = np.abs(xb).argmax(axis=-1)
+    assert np.all(np.abs(np.take_along_axis(qb, top[..., None], -1)) == 127)
+    order = np.argsort(xb, axis=-1, kind="stable")
+    assert np.all(np.diff(np.take_along_axis(qb, order, -1), axis=-1) >= 0)
+
+
+def _brute_w4a8(blocks, q, d):
+    """Exact W4A8 y and den as Fractions, decoded here (split-half rule)."""
+    out, nb, _ = blocks.shape
+    n = q.shape[0]
+    y = [[Fraction(0)] * out for _ in range(n)]
+    den = [[Fraction(0)] * out for _ in range(n)]
+    for o in range(out):
+        for t in range(n):
+            acc = mag = Fraction(0)
+            for b in range(nb):
+                blk = [int(v) for v in blocks[o, b]]
+                dw = _f16_bits_to_fraction(blk[0], blk[1])
+                dx = Fraction(float(d[t, b]))
+                codes = [(blk[2 + i] & 0x0F) for i in range(16)] + \
+                        [(blk[2 + i] >> 4) for i in range(16)]
+                s = sum((c - 8) * int(q[t, 32 * b + i]) for i, c in enumerate(codes))
+                a = sum(abs((c - 8) * int(q[t, 32 * b + i])) for i, c in enumerate(codes))
+                acc += dw * dx * s
+                mag += abs(dw * dx) * a
+            y[t][o], den[t][o] = acc, mag
+    return y, den
+
+
+@pytest.mark.parametrize("n,out,in_", [(1, 3, 32), (2, 5, 64), (3, 4, 96)])
+def test_w4a8_brute_force(n, out, in_):
+    blk = synth.make_blocks(out, in_, seed=out + in_)
+    x = synth.make_x(n, in_, seed=n)
+    q, d = oracle.quantize_x8(x)
+    y, den = oracle.matmul_w4a8(blk, q, d, out, in_)
+    yb, denb = _brute_w4a8(blk.reshape(out, in_ // 32, 18), q, d)
+    for t in range(n):
+        for o in range(out):
+            assert abs(Fraction(y[t, o]) - yb[t][o]) <= Fraction(1e-12) * denb[t][o]
+            assert abs(Fraction(den[t, o]) - denb[t][o]) <= Fraction(1e-12) * denb[t][o]
+
+
+def test_w4a8_equals_float_product_on_dequantized_activations():
+    """The W4A8 result is the plain product of W with x-hat = q * d."""
+    out, in_, n = 300, 1024, 3
+    blk = synth.make_blocks(out, in_, seed=3)
+    x = synth.make_x(n, in_, seed=4)
+    q, d = oracle.quantize_x8(x)
+    y, den = oracle.matmul_w4a8(blk, q, d, out, in_)
+    xhat = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    w = numpy_dequant(blk.reshape(out, in_ // 32, 18))
+    ref = xhat @ w.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * den + 1e-300)
+    assert np.allclose(den, np.abs(xhat) @ np.abs(w).T, rtol=1e-12, atol=0)
+
+
+def test_w4a8_zero_codes_and_quantization_error_bound():
+    out, in_ = 64, 512
+    x = synth.make_x(2, in_, seed=9)
+    q, d = oracle.quantize_x8(x)
+    z = synth.constant_blocks(out, in_, 0x3C00, 0x88)        # every weight 0
+    y0, _ = oracle.matmul_w4a8(z, q, d, out, in_)
+    assert not y0.any()
+    blk = synth.make_blocks(out, in_, seed=10)
+    y8, _ = oracle.matmul_w4a8(blk, q, d, out, in_)
+    yf, _ = oracle.matmul(blk, x, out, in_)
+    w = numpy_dequant(blk.reshape(out, in_ // 32, 18))
+    # each activation moves by at most d/2: |y8 - y| <= sum_k |w_k| d_b(k) / 2
+    half = np.repeat(d.astype(np.float64), 32, axis=1) * (0.5 + 1e-5)
+    assert np.all(np.abs(y8 - yf) <= half @ np.abs(w).T + 1e-12)
