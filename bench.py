@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--grouped", action="store_true",
                     help="block_decode: run the projections as grouped launches "
                          "(Q,K,V | O | gate,up | down)")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="decode workloads: int8 activations (q4_0_quantize_x8 + "
+                         "q4_0_matmul_w4a8 per linear)")
     ap.add_argument("--argmax", action="store_true",
                     help="decode workloads: q4_0_matmul_argmax with no y stored")
     ap.add_argument("--quick", action="store_true",
@@ -102,14 +105,16 @@ GRAPH_STEPS = 100   # steps recorded in one HIP graph
 BLOCK_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
-def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None, argmax=False):
+def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None, argmax=False,
+          w4a8=False):
     """Time `steps` steps (each step = every case once, on its next weight
     copy) between two events on the launch stream; return ms per step.
 
     With `groups` (lists of case indices) each group runs as one
     q4_0_matmul_grouped call whose linears all read the group's first x.
     With `argmax` each case runs as q4_0_matmul_argmax with no y stored (the
-    greedy pick of a logit head).
+    greedy pick of a logit head).  With `w4a8` each case quantizes its x to
+    int8 (q4_0_quantize_x8) and runs q4_0_matmul_w4a8 on the codes.
 
     With graph=True the launches are recorded once in a HIP graph that walks
     every weight copy (a multiple of GRAPH_STEPS steps) and the graph is
@@ -126,8 +131,17 @@ def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None, argm
         for c in cases:
             c.mv = torch.empty(c.n, dtype=torch.float32, device="cuda")
             c.mi = torch.empty(c.n, dtype=torch.int32, device="cuda")
+    if w4a8:
+        for c in cases:
+            c.q8 = torch.empty((c.n, c.in_), dtype=torch.int8, device="cuda")
+            c.d8 = torch.empty((c.n, c.in_ // 32), dtype=torch.float32, device="cuda")
 
     def step(i, sh):
+        if w4a8:
+            for c in cases:
+                q4.q4_0_quantize_x8(c.x, c.xcode, c.q8, c.d8, c.n, c.in_, sh)
+                q4.q4_0_matmul_w4a8(c.packed[i % ncopy], c.q8, c.d8, c.y, c.n, c.out, c.in_, sh)
+            return
         if argmax:
             for c in cases:
                 q4.q4_0_matmul_argmax(c.packed[i % ncopy], c.x, c.xcode, None, c.n, c.out,
@@ -210,14 +224,15 @@ def traffic_for(workload, kernel_name):
 
 
 def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, groups=None,
-                argmax=False):
+                argmax=False, w4a8=False):
     total_w = sum(q4.q4_0_blocks_bytes(o, i) for o, i in linears)
     copies = copies_for(total_w)
     cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies)
              for k, (o, i) in enumerate(linears)]
-    ms, steps = timed(torch, q4, cases, kernel, steps, warmup, groups=groups, argmax=argmax)
+    ms, steps = timed(torch, q4, cases, kernel, steps, warmup, groups=groups, argmax=argmax,
+                      w4a8=w4a8)
     ms_eager, _ = timed(torch, q4, cases, kernel, min(steps, 200), 5, graph=False,
-                        groups=groups, argmax=argmax)
+                        groups=groups, argmax=argmax, w4a8=w4a8)
     gbs = total_w / (ms * 1e-3) / 1e9
     kern = sorted({q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, o, i) if kernel == 0 else kernel]
                    for o, i in linears})
@@ -226,7 +241,8 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, group
            "weight_bytes": total_w, "GB/s": round(gbs, 1),
            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "kernels": kern,
            "launches_per_step": len(linears) if groups is None else len(groups),
-           "grouped": groups is not None, "argmax": argmax, "rotation_copies": copies}
+           "grouped": groups is not None, "argmax": argmax, "w4a8": w4a8,
+           "rotation_copies": copies}
     del cases
     torch.cuda.empty_cache()
     return res
@@ -308,10 +324,10 @@ def main():
             names = [l.name for l in wl.linears]
             groups = [[names.index(nm) for nm in grp] for grp in BLOCK_GROUPS]
         ms, steps_done = timed(torch, q4, cases, kernel, args.steps, args.warmup, groups=groups,
-                               argmax=args.argmax)
+                               argmax=args.argmax, w4a8=args.w4a8)
         ms_eager, _ = timed(torch, q4, cases, kernel, min(args.steps, 500), 5, graph=False,
-                            groups=groups, argmax=args.argmax)
-        parity = None if args.argmax else max(
+                            groups=groups, argmax=args.argmax, w4a8=args.w4a8)
+        parity = None if (args.argmax or args.w4a8) else max(
             parity_check(q4, __import__("oracle"), synth, c, seed=k) for k, c in enumerate(cases))
         value = total_w / (ms * 1e-3) / 1e9
         unit = "GB/s"
@@ -325,7 +341,7 @@ def main():
                "weight_bytes_per_step": total_w,
                "algorithmic_bytes_per_launch": per_launch_bytes,
                "timing": "HIP graph replay of the step's launches",
-               "grouped": groups is not None, "argmax": args.argmax,
+               "grouped": groups is not None, "argmax": args.argmax, "w4a8": args.w4a8,
                "ms_per_step_eager": round(ms_eager, 6)}
         dtype = "f32"
         del cases
@@ -361,6 +377,13 @@ def main():
                                                       kk, 300, 20))
                 extra["mid_n"].append(decode_line(torch, q4, synth, "block_decode", blk, nn,
                                                   q4.KERNEL_AUTO, 200, 20, groups=bgroups))
+            # W4A8: activations quantized to int8 per 32-value block, then the
+            # integer product (both launches timed)
+            extra["w4a8"] = [
+                decode_line(torch, q4, synth, "ffn_up_decode", up, 1, 0, 1000, 50, w4a8=True),
+                decode_line(torch, q4, synth, "block_decode", blk, 4, 0, 200, 20, w4a8=True),
+                decode_line(torch, q4, synth, "logit_head", [(151936, 2560)], 1, 0, 200, 20,
+                            w4a8=True)]
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
 
     if args.calib_copy:

@@ -77,6 +77,8 @@ _SIGS = {
     "q4_0_release_workspaces": (_int, []),
     "q4_0_matmul_grouped": (_int, [_vp, _int, _int, _i64, _vp]),
     "q4_0_matmul_argmax": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "q4_0_quantize_x8": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _vp]),
+    "q4_0_matmul_w4a8": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -192,6 +194,36 @@ def matmul_argmax(packed, x, out: int, y=None, stream=None):
     mi = torch.empty(n, dtype=torch.int32, device=x.device)
     q4_0_matmul_argmax(packed, x, dtype_code(x), y, n, out, in_, mv, mi, stream)
     return mv, mi
+
+
+def q4_0_quantize_x8(x, x_dtype: int, q, d, n: int, in_: int, stream=None) -> None:
+    _check(_lib.q4_0_quantize_x8(_ptr(x), x_dtype, _ptr(q), _ptr(d), n, in_,
+                                 _stream(stream, x, q, d)), "q4_0_quantize_x8")
+
+
+def q4_0_matmul_w4a8(packed, q, d, y, n: int, out: int, in_: int, stream=None) -> None:
+    _check(_lib.q4_0_matmul_w4a8(_ptr(packed), _ptr(q), _ptr(d), _ptr(y), n, out, in_,
+                                 _stream(stream, packed, q, y)), "q4_0_matmul_w4a8")
+
+
+def quantize_x8(x, stream=None):
+    """(q int8 [n x in], d float32 [n x in/32]) of a 2-D CUDA tensor x."""
+    import torch
+    n, in_ = x.shape
+    q = torch.empty((n, in_), dtype=torch.int8, device=x.device)
+    d = torch.empty((n, in_ // 32), dtype=torch.float32, device=x.device)
+    q4_0_quantize_x8(x, dtype_code(x), q, d, n, in_, stream)
+    return q, d
+
+
+def matmul_w4a8(packed, q, d, out: int, y=None, stream=None):
+    """y [n x out] of the W4A8 product on quantized activations (q, d)."""
+    import torch
+    n, in_ = q.shape
+    if y is None:
+        y = torch.empty((n, out), dtype=torch.float32, device=q.device)
+    q4_0_matmul_w4a8(packed, q, d, y, n, out, in_, stream)
+    return y
 
 
 def q4_0_select_kernel(n: int, out: int, in_: int, x_dtype: int = F32) -> int:

@@ -203,6 +203,44 @@ int q4_0_matmul_argmax(const void *packed, const void *x, int x_dtype, float *y,
                                                ws, s));
 }
 
+int q4_0_quantize_x8(const void *x, int x_dtype, int8_t *q, float *d, int64_t n, int64_t in,
+                     void *stream) {
+    const int st = check_shape(n, 1, in);
+    if (st != Q4_0_OK) return st;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    if (!x || !q || !d) return Q4_0_ENULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(d, 4)) return Q4_0_EALIGN;
+    const size_t xbytes = (size_t)n * (size_t)in * (size_t)elem_bytes(x_dtype);
+    const size_t qbytes = (size_t)n * (size_t)in, dbytes = (size_t)n * (size_t)(in / 32) * 4u;
+    if (overlaps(q, qbytes, x, xbytes) || overlaps(d, dbytes, x, xbytes) ||
+        overlaps(q, qbytes, d, dbytes))
+        return Q4_0_EALIAS;
+    return map_hip(q4::launch_quantize_x8(x, x_dtype == Q4_0_F16, q, d, n, in,
+                                          (hipStream_t)stream));
+}
+
+int q4_0_matmul_w4a8(const void *packed, const int8_t *q, const float *d, float *y, int64_t n,
+                     int64_t out, int64_t in, void *stream) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (!packed || !q || !d || !y) return Q4_0_ENULL;
+    if (!aligned(packed, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4))
+        return Q4_0_EALIGN;
+    const size_t ybytes = (size_t)n * (size_t)out * 4u;
+    if (overlaps(y, ybytes, packed, q4_0_packed_bytes(out, in)) ||
+        overlaps(y, ybytes, q, (size_t)n * (size_t)in) ||
+        overlaps(y, ybytes, d, (size_t)n * (size_t)(in / 32) * 4u))
+        return Q4_0_EALIAS;
+    if (!q4::w4a8_supports(n, out, in)) return Q4_0_EUNSUPPORTED;
+    const hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (q4::w4a8_workspace_bytes(n, out, in) > 0) {
+        const int wst = get_workspace(s, &ws);
+        if (wst != Q4_0_OK) return wst;
+    }
+    return map_hip(q4::launch_gemv_w4a8(packed, q, d, y, n, out, in, ws, s));
+}
+
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream) {
     if (!linears) return Q4_0_ENULL;

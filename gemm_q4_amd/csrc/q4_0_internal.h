@@ -62,6 +62,16 @@ hipError_t launch_gemv_mfma_argmax(const void *packed, const void *x, int x_f16,
                                    int64_t n, int64_t out, int64_t in, float *max_val,
                                    int32_t *max_idx, void *ws, hipStream_t stream);
 
+// W4A8: activations quantized per 32-value block to int8 (q, d), product on
+// the integer matrix cores with the offset-8 correction; n <= 64 (16-row
+// launches).
+hipError_t launch_quantize_x8(const void *x, int x_f16, int8_t *q, float *d, int64_t n,
+                              int64_t in, hipStream_t stream);
+bool w4a8_supports(int64_t n, int64_t out, int64_t in);
+size_t w4a8_workspace_bytes(int64_t n, int64_t out, int64_t in);
+hipError_t launch_gemv_w4a8(const void *packed, const int8_t *q, const float *d, float *y,
+                            int64_t n, int64_t out, int64_t in, void *ws, hipStream_t stream);
+
 // Prefill kernel: binary16 MFMA on d * (q - 8) rounded to binary16.  When the
 // tiles cannot fill the device it splits K and needs the workspace.
 bool gemm_supports(int64_t n, int64_t out, int64_t in, int x_f16);

@@ -178,6 +178,33 @@ int q4_0_matmul_argmax(const void *packed, const void *x, int x_dtype, float *y,
                        int64_t out, int64_t in, float *max_val, int32_t *max_idx,
                        void *stream);
 
+/* W4A8, the step before the product: quantize activations to 8-bit
+ * integers, one scale per 32 values of a row (the weights' block size).
+ * rembed "Architecture", "int8 quantization" (activations quantized, an
+ * integer dot, an offset correction in the epilogue, an exact integer
+ * reference); goinfer primer ch. 10 (the quantized dot on 8-bit integer
+ * dot-product hardware).  The pages do not give the scale granularity; this
+ * library reads it as per 32-value block:
+ *     d[t][b] = max_k |x[t][32b + k]| / 127              (float32 division)
+ *     q[t][k] = x[t][k] / d[t][b], rounded to nearest, ties to even
+ *               (float32 division), or 0 when d is not positive and finite.
+ *   x : [n x in] float32 or binary16, 16-byte aligned.
+ *   q : [n x in] int8, 16-byte aligned;  d : [n x in/32] float32.
+ * q and d are bit-identical to any correctly rounded float32 evaluation of
+ * these formulas. */
+int q4_0_quantize_x8(const void *x, int x_dtype, int8_t *q, float *d, int64_t n, int64_t in,
+                     void *stream);
+
+/* W4A8 product on quantized activations (q, d from q4_0_quantize_x8):
+ *     y[t][o] = sum_b dw[o][b] * d[t][b] * sum_{k in b} (qw[o][k] - 8) * q[t][k]
+ * with exact integer block sums on the integer matrix cores (the offset 8
+ * subtracted as 8 * sum_k q, rembed's colSum correction) and float32 scaling
+ * and accumulation: |y - y_exact| <= 1e-4 * sum_b |dw d| sum_k |(qw-8) q|.
+ * n <= 64 (one launch per 16 rows).  y: [n x out] float32, overwritten,
+ * overlapping neither W, q nor d. */
+int q4_0_matmul_w4a8(const void *packed, const int8_t *q, const float *d, float *y, int64_t n,
+                     int64_t out, int64_t in, void *stream);
+
 /* The kernel q4_0_matmul would run for this call shape (a Q4_0_KERNEL_*
  * value), or a negative status for an invalid shape.  Host only. */
 int q4_0_select_kernel(int64_t n, int64_t out, int64_t in, int x_dtype);

@@ -201,3 +201,20 @@ def test_argmax_validation():
     assert status_of(am, A16, B16, q4.F32, C16, 2, 10, 64, D16, D16 + 4, 0) == q4.EALIAS
     assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, C16 + 8, E16, 0) == q4.EALIAS
     assert status_of(am, A16, B16, q4.F32, C16, 65, 10, 64, D16, E16, 0) == q4.EUNSUPPORTED
+
+
+def test_w4a8_validation():
+    qx, mm = q4.q4_0_quantize_x8, q4.q4_0_matmul_w4a8
+    D16 = 1 << 38
+    assert status_of(qx, A16, q4.F32, B16, C16, 1, 48, 0) == q4.ESHAPE
+    assert status_of(qx, A16, 9, B16, C16, 1, 64, 0) == q4.EINVAL
+    assert status_of(qx, 0, q4.F32, B16, C16, 1, 64, 0) == q4.ENULL
+    assert status_of(qx, A16, q4.F32, B16 + 4, C16, 1, 64, 0) == q4.EALIGN
+    assert status_of(qx, A16, q4.F32, A16 + 16, C16, 1, 64, 0) == q4.EALIAS
+    assert status_of(qx, A16, q4.F32, B16, B16 + 16, 1, 64, 0) == q4.EALIAS
+    assert status_of(mm, A16, B16, C16, D16, 1, 10, 48, 0) == q4.ESHAPE
+    assert status_of(mm, A16, 0, C16, D16, 1, 10, 64, 0) == q4.ENULL
+    assert status_of(mm, A16, B16 + 8, C16, D16, 1, 10, 64, 0) == q4.EALIGN
+    assert status_of(mm, A16, B16, C16, B16 + 32, 1, 10, 64, 0) == q4.EALIAS
+    assert status_of(mm, A16, B16, C16, A16 + 64, 1, 10, 64, 0) == q4.EALIAS
+    assert status_of(mm, A16, B16, C16, D16, 65, 10, 64, 0) == q4.EUNSUPPORTED

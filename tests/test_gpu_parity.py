@@ -486,3 +486,76 @@ def test_argmax_rejects_n_above_64():
     with pytest.raises(q4.Q4Error) as e:
         q4.matmul_argmax(p, x, 16)
     assert e.value.status == q4.EUNSUPPORTED
+
+
+# -------------------------------------------------------------------- W4A8
+# The quantizer is integer work decided by float32: bit-exact against the
+# oracle's.  The product is held to its own definition on the same codes:
+# exact integer block sums, float32 scaling and accumulation, so
+# |y - y_w4a8| <= (nb + 2) 2^-24 sum_b |dw d| sum_k |(qw-8) q|, below 1e-4.
+TOL_W4A8 = 1e-4
+
+
+def _quantized_pair(x):
+    xd = to_dev(x)
+    q, d = q4.quantize_x8(xd)
+    torch.cuda.synchronize()
+    qo, do = oracle.quantize_x8(x.astype(np.float32))
+    qg, dg = q.cpu().numpy(), d.cpu().numpy()
+    assert np.array_equal(qg, qo)
+    assert np.array_equal(np.isnan(dg), np.isnan(do))
+    assert np.array_equal(dg[~np.isnan(dg)].view(np.uint32), do[~np.isnan(do)].view(np.uint32))
+    return q, d, qo, do
+
+
+@pytest.mark.parametrize("scale", [1e-30, 1e-3, 1.0, 3e2, 1e30])
+@pytest.mark.parametrize("xdt", [np.float32, np.float16], ids=["xf32", "xf16"])
+def test_quantize_x8_bit_exact(scale, xdt):
+    x = (synth.make_x(5, 4096, seed=int(np.log10(scale) + 40)) * scale)
+    if xdt == np.float16 and not 1e-4 < scale < 1e4:
+        pytest.skip("outside binary16 range")
+    _quantized_pair(x.astype(xdt))
+
+
+def test_quantize_x8_ties_zero_and_nan_blocks():
+    x = np.zeros((3, 128), np.float32)
+    x[0, :8] = [127.0, 0.5, 1.5, 2.5, -1.5, -127.0, 63.5, -0.49]
+    x[1, 32:64] = synth.make_x(1, 32, seed=1)
+    x[1, 40] = np.nan
+    x[2, 64:96] = np.linspace(-3, 3, 32, dtype=np.float32)
+    _, _, qo, _ = _quantized_pair(x)
+    assert qo[0, :8].tolist() == [127, 0, 2, 2, -2, -127, 64, 0]
+
+
+@pytest.mark.parametrize("n,out,in_", [(1, 300, 160), (3, 37, 4128), (8, 64, 9728),
+                                       (16, 130, 1024), (20, 100, 256), (1, 1, 32)])
+def test_w4a8_parity(n, out, in_):
+    blk = synth.make_blocks(out, in_, seed=out + n)
+    x = synth.make_x(n, in_, seed=in_ + n)
+    q, d, qo, do = _quantized_pair(x)
+    p = packed_from_blocks(blk, out, in_)
+    y = q4.matmul_w4a8(p, q, d, out)
+    torch.cuda.synchronize()
+    y8, den8 = oracle.matmul_w4a8(blk, qo, do, out, in_)
+    assert oracle.max_ratio(y.cpu().numpy(), y8, den8) <= TOL_W4A8
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_w4a8_ffn_up_full_size_and_quantization_error(n):
+    """FFN-up 9728 x 2560 at full size: parity on every row, and the error
+    against the float32-activation product is reported (and bounded by the
+    activations' half-step: |y - y_ref| <= sum_k |w_k| d_b / 2)."""
+    out, in_ = 9728, 2560
+    blk = synth.make_blocks(out, in_, seed=0)
+    x = synth.make_x(n, in_, seed=1000)
+    q, d, qo, do = _quantized_pair(x)
+    y = q4.matmul_w4a8(packed_from_blocks(blk, out, in_), q, d, out).cpu().numpy()
+    y8, den8 = oracle.matmul_w4a8(blk, qo, do, out, in_)
+    assert oracle.max_ratio(y, y8, den8) <= TOL_W4A8
+    rows = np.arange(0, out, 97)
+    yf, denf = oracle.matmul(blk, x, out, in_, rows=rows)
+    w = oracle.dequantize(blk, out, in_)[rows].astype(np.float64)
+    half = np.repeat(do.astype(np.float64), 32, axis=1) * (0.5 + 1e-5)
+    assert np.all(np.abs(y[:, rows] - yf) <= half @ np.abs(w).T + TOL_W4A8 * den8[:, rows])
+    print(f"W4A8 vs float32 activations, n={n}: max ratio "
+          f"{oracle.max_ratio(y[:, rows], yf, denf):.2e}")
