@@ -234,8 +234,9 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, group
     ms_eager, _ = timed(torch, q4, cases, kernel, min(steps, 200), 5, graph=False,
                         groups=groups, argmax=argmax, w4a8=w4a8)
     gbs = total_w / (ms * 1e-3) / 1e9
-    kern = sorted({q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, o, i) if kernel == 0 else kernel]
-                   for o, i in linears})
+    kern = ["w4a8"] if w4a8 else sorted(
+        {q4.KERNEL_NAMES[q4.q4_0_select_kernel(n, o, i) if kernel == 0 else kernel]
+         for o, i in linears})
     res = {"workload": name, "n": n, "ms_per_step": round(ms, 5), "steps": steps,
            "ms_per_step_eager": round(ms_eager, 5),
            "weight_bytes": total_w, "GB/s": round(gbs, 1),

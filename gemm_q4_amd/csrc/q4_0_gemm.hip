@@ -40,11 +40,11 @@
 #include <type_traits>
 
 #include "q4_0_device.h"
+#include "q4_0_dma.h"
 #include "q4_0_internal.h"
 
 namespace q4 {
 
-typedef float f16x_t __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmBM = 128;                 // activation rows per workgroup
 constexpr int kGemmBN = 128;                 // weight rows per workgroup
@@ -101,30 +101,7 @@ __device__ __forceinline__ u4_t to_half8(const X8 &v) {
     return h;
 }
 
-// Direct copy of 16 bytes per lane from global memory into LDS (no register
-// round trip): the wave's 64 lanes fill 1 KB at `lds` (wave-uniform), lane i
-// at lds + 16 i.  Written as inline assembly on purpose: the compiler does not
-// know which LDS bytes such a copy writes, so for its own copy instruction it
-// waits for every outstanding copy before each later LDS read, which would
-// drain the multi-stage pipeline below.  Here the copies are invisible to it
-// and the kernel waits for them explicitly (vector-memory count, then a
-// barrier) before reading a stage.  M0 holds the LDS base; one wait state
-// separates its write from the copy.
-__device__ __forceinline__ void dma16(const void *src, uint8_t *lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(base)
-                 : "memory", "m0");
-}
 
-__device__ const u4_t kZeroPiece = {0u, 0u, 0u, 0u};
-
-// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt left
-// free): vmcnt is bits 3:0 and 15:14 of the immediate.
-#define Q4_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
-#define Q4_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 
 template <typename XT>
@@ -522,6 +499,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
 }
 
 // y of the split tiles = sum of their K slices' partial tiles, in slice order.
+constexpr int kReduceBatch = 8;   // slice loads in flight per thread
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ part,
                                                           float *__restrict__ y, int n, int out,
                                                           int nm, int full, int rem, int split) {
@@ -534,11 +512,25 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restric
         const int t = full + r;
         const int grow = (t % nm) * kGemmBM + row, gcol = (t / nm) * kGemmBN + col;
         if (grow >= n) continue;
-        float4 s4 = *reinterpret_cast<const float4 *>(part + (int64_t)r * kGemmBM * kGemmBN + local);
-        for (int q = 1; q < split; ++q) {
-            const float4 v = *reinterpret_cast<const float4 *>(
-                part + ((int64_t)q * rem + r) * kGemmBM * kGemmBN + local);
-            s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
+        // the slices' loads are issued in batches (indices past the last
+        // slice re-read it and are not added), then added in slice order
+        float4 s4 = {0.f, 0.f, 0.f, 0.f};
+        for (int q0 = 0; q0 < split; q0 += kReduceBatch) {
+            float4 v[kReduceBatch];
+#pragma unroll
+            for (int b = 0; b < kReduceBatch; ++b) {
+                const int q = q0 + b < split ? q0 + b : split - 1;
+                v[b] = *reinterpret_cast<const float4 *>(
+                    part + ((int64_t)q * rem + r) * kGemmBM * kGemmBN + local);
+            }
+#pragma unroll
+            for (int b = 0; b < kReduceBatch; ++b) {
+                const bool on = q0 + b < split;
+                s4.x += on ? v[b].x : 0.f;
+                s4.y += on ? v[b].y : 0.f;
+                s4.z += on ? v[b].z : 0.f;
+                s4.w += on ? v[b].w : 0.f;
+            }
         }
         float *yp = y + (int64_t)grow * out + gcol;
         const float vv[4] = {s4.x, s4.y, s4.z, s4.w};

@@ -575,6 +575,7 @@ struct ReduceArgs {
     uint2 *amax;         // per-workgroup (max, index) pairs of a single linear, or null
 };
 
+constexpr int kReduceBatch = 8;   // slice loads in flight per thread
 template <int NT>
 __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs args) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -595,9 +596,19 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
         const int rr = (int)(e & 15);
         const int tt = (int)((e >> 4) % NT);
         const int64_t t = (e >> 4) / NT;
+        // the slices' loads are issued in batches (indices past the last
+        // slice re-read it and are not added), then added in slice order
         float s = 0.0f;
-        for (int64_t q = 0; q < L.slices; ++q)
-            s += L.part[((q * L.tiles + t) * kMaxRows + tt) * 16 + rr];
+        for (int64_t q0 = 0; q0 < L.slices; q0 += kReduceBatch) {
+            float v[kReduceBatch];
+#pragma unroll
+            for (int b = 0; b < kReduceBatch; ++b) {
+                const int64_t q = q0 + b < L.slices ? q0 + b : L.slices - 1;
+                v[b] = L.part[((q * L.tiles + t) * kMaxRows + tt) * 16 + rr];
+            }
+#pragma unroll
+            for (int b = 0; b < kReduceBatch; ++b) s += q0 + b < L.slices ? v[b] : 0.0f;
+        }
         const int64_t row = t * kTileRows + rr;
         if (row < L.out) {
             if (L.y) L.y[(int64_t)tt * L.out + row] = s;

@@ -66,7 +66,8 @@ extern "C" {
                                    split into high and low binary16 parts;
                                    9..16: one binary16 part; 17..64: 16-row
                                    slices, one launch each                    */
-#define Q4_0_KERNEL_GEMM 3      /* prefill: tiles dequantized to fp16, MFMA   */
+#define Q4_0_KERNEL_GEMM 3      /* prefill: 128 x 128 tiles, weights decoded
+                                   to binary16, MFMA                          */
 
 /* Largest sizes accepted (32-bit grid and index limits). */
 #define Q4_0_MAX_IN 1048576
