@@ -249,7 +249,25 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, group
     return res
 
 
+def mfma_loop_peak(torch, q4, reps=3):
+    """Sustained rate of back-to-back v_mfma_f32_32x32x16_f16 on every SIMD
+    (the library's measurement aid), best of `reps` launches, in TFLOP/s."""
+    wgs, iters = 256, 4000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for _ in range(reps + 1):                 # the first launch warms the clock up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flops = q4.q4_0_mfma_loop(sink, wgs, iters, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return round(best, 1)
+
+
 def prefill_line(torch, q4, synth, kernel, steps, warmup):
+    loop_peak = mfma_loop_peak(torch, q4)
     res = []
     for li, (o, i) in enumerate([(9728, 2560), (2560, 9728)]):
         c = Case(torch, q4, synth, o, i, 512, "f16", seed=li, copies=4)
@@ -257,6 +275,7 @@ def prefill_line(torch, q4, synth, kernel, steps, warmup):
         tfs = c.flops / (ms * 1e-3) / 1e12
         res.append({"linear": f"{o}x{i}", "n": 512, "ms_per_step": round(ms, 5),
                     "TFLOP/s": round(tfs, 2), "frac_mfma_f16": round(tfs / F16_MFMA_PEAK_TFS, 4),
+                    "mfma_loop_TFLOP/s": loop_peak, "frac_mfma_loop": round(tfs / loop_peak, 4),
                     "kernel": q4.KERNEL_NAMES[q4.q4_0_select_kernel(512, o, i, q4.F16)
                                               if kernel == 0 else kernel]})
         del c

@@ -79,6 +79,7 @@ _SIGS = {
     "q4_0_matmul_argmax": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "q4_0_quantize_x8": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _vp]),
     "q4_0_matmul_w4a8": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_0_mfma_loop": (_int, [_vp, _i64, _i64, ctypes.POINTER(_i64), _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -237,6 +238,14 @@ def q4_0_kernel_supports(kernel: int, n: int, out: int, in_: int,
         return False
     _check(st, "q4_0_kernel_supports")
     return True
+
+
+def q4_0_mfma_loop(sink, workgroups: int, iters: int, stream=None) -> int:
+    """Enqueue the MFMA loop measurement aid; returns the launch's flops."""
+    flops = _i64(0)
+    _check(_lib.q4_0_mfma_loop(_ptr(sink), workgroups, iters, ctypes.byref(flops),
+                               _stream(stream, sink)), "q4_0_mfma_loop")
+    return flops.value
 
 
 def q4_0_release_workspaces() -> None:

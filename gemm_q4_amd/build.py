@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libq4_0.so")
 SOURCES = ["q4_0_api.hip", "q4_0_repack.hip", "q4_0_gemv_dpp.hip",
-           "q4_0_gemv_mfma.hip", "q4_0_gemv_w4a8.hip", "q4_0_gemm.hip"]
+           "q4_0_gemv_mfma.hip", "q4_0_gemv_w4a8.hip", "q4_0_gemm.hip",
+           "q4_0_calibrate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -301,6 +301,14 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
     return Q4_0_OK;
 }
 
+int q4_0_mfma_loop(float *sink, int64_t workgroups, int64_t iters, int64_t *flops,
+                   void *stream) {
+    if (!sink || !flops) return Q4_0_ENULL;
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > 1000000) return Q4_0_EINVAL;
+    *flops = q4::mfma_loop_flops(workgroups, iters);
+    return map_hip(q4::launch_mfma_loop(sink, workgroups, iters, (hipStream_t)stream));
+}
+
 const char *q4_0_strerror(int status) {
     switch (status) {
     case Q4_0_OK: return "success";

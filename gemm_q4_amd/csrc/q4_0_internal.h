@@ -79,4 +79,8 @@ size_t gemm_workspace_bytes(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y,
                        int64_t n, int64_t out, int64_t in, void *ws, hipStream_t stream);
 
+// Measurement aid: back-to-back v_mfma_f32_32x32x16_f16 on every SIMD.
+int64_t mfma_loop_flops(int64_t workgroups, int64_t iters);
+hipError_t launch_mfma_loop(float *sink, int64_t workgroups, int64_t iters, hipStream_t stream);
+
 }  // namespace q4

@@ -215,6 +215,18 @@ int q4_0_select_kernel(int64_t n, int64_t out, int64_t in, int x_dtype);
 int q4_0_kernel_supports(int kernel, int64_t n, int64_t out, int64_t in,
                          int x_dtype);
 
+/* Measurement aid for benchmarks, not a product call: benchmarks state the
+ * large-n kernel's MFMA utilisation against the published peak and against
+ * this loop's measured rate (under a sustained matrix load the part runs
+ * below its boost clock).  Enqueues `workgroups` workgroups of four waves, one wave per
+ * SIMD, each issuing `iters` x 8 independent v_mfma_f32_32x32x16_f16 back to
+ * back, and writes one checksum per thread to sink[workgroups * 256] (device
+ * float32, caller-owned).  *flops receives the floating-point operations the
+ * launch performs (host pointer); the caller times the launch on `stream`.
+ * 1 <= workgroups <= 65536 and 1 <= iters <= 1e6, else Q4_0_EINVAL. */
+int q4_0_mfma_loop(float *sink, int64_t workgroups, int64_t iters, int64_t *flops,
+                   void *stream);
+
 /* Static text for a status code. */
 const char *q4_0_strerror(int status);
 

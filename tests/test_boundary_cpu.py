@@ -218,3 +218,12 @@ def test_w4a8_validation():
     assert status_of(mm, A16, B16, C16, B16 + 32, 1, 10, 64, 0) == q4.EALIAS
     assert status_of(mm, A16, B16, C16, A16 + 64, 1, 10, 64, 0) == q4.EALIAS
     assert status_of(mm, A16, B16, C16, D16, 65, 10, 64, 0) == q4.EUNSUPPORTED
+
+
+def test_mfma_loop_validation():
+    f = q4.q4_0_mfma_loop
+    assert status_of(f, 0, 1, 1, 0) == q4.ENULL
+    assert status_of(f, A16, 0, 1, 0) == q4.EINVAL
+    assert status_of(f, A16, 65537, 1, 0) == q4.EINVAL
+    assert status_of(f, A16, 1, 0, 0) == q4.EINVAL
+    assert status_of(f, A16, 1, 1000001, 0) == q4.EINVAL

@@ -559,3 +559,28 @@ def test_w4a8_ffn_up_full_size_and_quantization_error(n):
     assert np.all(np.abs(y[:, rows] - yf) <= half @ np.abs(w).T + TOL_W4A8 * den8[:, rows])
     print(f"W4A8 vs float32 activations, n={n}: max ratio "
           f"{oracle.max_ratio(y[:, rows], yf, denf):.2e}")
+
+
+def test_mfma_loop_aid_checksums_and_flops():
+    """The MFMA measurement aid: every thread's checksum is the exact sum of
+    its accumulator values, iters x 8 copies of one 32 x 32 x 16 product of
+    the fixed operands (multiples of 2^-20 below 8 with 16 iterations, so
+    float32 holds every partial sum exactly), and the reported flops match
+    the launch."""
+    wgs, iters = 3, 16
+    sink = torch.full((wgs * 256,), float("nan"), device=DEV)
+    flops = q4.q4_0_mfma_loop(sink, wgs, iters)
+    torch.cuda.synchronize()
+    assert flops == wgs * 4 * iters * 8 * 2 * 32 * 32 * 16
+    # operands: A[r][k] = ((r + k % 8) & 15) / 1024, B[k][c] = ((3c + k % 8) & 15) / 1024
+    k = np.arange(16)
+    A = ((np.arange(32)[:, None] + k[None, :] % 8) & 15) / 1024.0
+    B = ((3 * np.arange(32)[None, :] + k[:, None] % 8) & 15) / 1024.0
+    D = A @ B
+    want = np.empty(64)
+    for lane in range(64):
+        h, c = lane // 32, lane % 32
+        rows = [8 * (v // 4) + 4 * h + v % 4 for v in range(16)]
+        want[lane] = 8 * iters * D[rows, c].sum()
+    got = sink.cpu().numpy().reshape(wgs * 4, 64)
+    assert np.array_equal(got, np.broadcast_to(want, got.shape).astype(np.float32))
