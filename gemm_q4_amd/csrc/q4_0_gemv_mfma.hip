@@ -55,8 +55,22 @@
 
 namespace q4 {
 
+// Workgroups a launch aims for.  Each workgroup stages (or, from kPrepMinN
+// rows on, loads as prepared fragments) the x of its whole K range once and
+// walks a run of tiles with it; from four rows on those fragments outweigh
+// one 16-row tile's weights, so short runs multiply the traffic.  Measured on
+// MI355X (graph replay): up to a few thousand tile-slices about one workgroup
+// per compute unit is best (FFN-up 9728 x 2560, n = 1/4/8: 6.0/8.8/10.1 us
+// against 6.3/9.9/11.3 us with one tile per workgroup); the 151936-row logit
+// head wants about four per compute unit (39 us against 44 us).
 #ifndef Q4_MFMA_TARGET_WGS
-#define Q4_MFMA_TARGET_WGS 1024      // about four workgroups per compute unit
+#define Q4_MFMA_TARGET_WGS 1024
+#endif
+#ifndef Q4_MFMA_TARGET_WGS_SMALL
+#define Q4_MFMA_TARGET_WGS_SMALL 256
+#endif
+#ifndef Q4_MFMA_MANY_TILES
+#define Q4_MFMA_MANY_TILES 4096
 #endif
 #ifndef Q4_MFMA_LDS_BUDGET
 #define Q4_MFMA_LDS_BUDGET (56 * 1024)
@@ -72,6 +86,8 @@ template <int NT> constexpr bool split_rows() { return NT <= 8; }
 template <int NT> constexpr int row_slots() { return NT <= 8 ? 2 * NT : NT; }
 static int64_t slots_for(int64_t n) { return n <= 8 ? 2 * n : n; }
 constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
+constexpr int kMfmaTargetWgsSmall = Q4_MFMA_TARGET_WGS_SMALL;
+constexpr int64_t kMfmaManyTiles = Q4_MFMA_MANY_TILES;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
 // x items (8 values each) a lane holds while it stages: caps groups per wave x n
 constexpr int kMaxStageItems = 10;
@@ -701,8 +717,11 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     p.per = (int)((p.gps + waves - 1) / waves);
     p.waves = (int)((p.gps + p.per - 1) / p.per);
     p.gpw = gpw_for(p.per, n, prep);
-    // about kMfmaTargetWgs workgroups in all, each walking a run of tiles
-    int64_t tpw = (L.tiles * p.slices + kMfmaTargetWgs - 1) / kMfmaTargetWgs;
+    // about kMfmaTargetWgs (or, for fewer tile-slices, kMfmaTargetWgsSmall)
+    // workgroups in all, each walking a run of tiles
+    const int64_t units = L.tiles * p.slices;
+    const int64_t target = units >= kMfmaManyTiles ? kMfmaTargetWgs : kMfmaTargetWgsSmall;
+    int64_t tpw = (units + target - 1) / target;
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
     p.gx = (L.tiles + tpw - 1) / tpw;
