@@ -273,6 +273,7 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
         probs[i] = {L.packed, L.x, L.y, L.out, L.in};
     }
     if (ws_total > q4::kWorkspaceBytes) one_launch = false;
+    if (one_launch && !q4::gemv_mfma_group_uniform(probs, count, n)) one_launch = false;
     const hipStream_t s = (hipStream_t)stream;
     if (!one_launch) {
         for (int i = 0; i < count; ++i) {

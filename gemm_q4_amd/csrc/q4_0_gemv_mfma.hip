@@ -92,12 +92,20 @@ constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per work
 // x items (8 values each) a lane holds while it stages: caps groups per wave x n
 constexpr int kMaxStageItems = 10;
 // Activation rows from which x is converted once per launch by a pre-pass
-// (xprep_kernel) instead of by every workgroup: measured on MI355X, the
-// per-workgroup conversion dominates a decode launch from a few rows on.
+// (xprep_kernel) instead of by every workgroup.  Measured on MI355X (graph
+// replay, workgroups walking runs of tiles): FFN-up 9728 x 2560 at n = 4/5/6
+// takes 8.0/8.9/14.6 us with per-workgroup conversion against 8.7/9.1/9.7 us
+// with the pre-pass; the 151936-row head at n = 4 takes 49 us against 46 us.
+// So the pre-pass from 6 rows, and from 4 rows for matrices of at least
+// kMfmaManyTiles tiles.
 #ifndef Q4_MFMA_PREP_MIN_N
-#define Q4_MFMA_PREP_MIN_N 4
+#define Q4_MFMA_PREP_MIN_N 6
+#endif
+#ifndef Q4_MFMA_PREP_MIN_N_LARGE
+#define Q4_MFMA_PREP_MIN_N_LARGE 4
 #endif
 constexpr int kPrepMinN = Q4_MFMA_PREP_MIN_N;
+constexpr int kPrepMinNLarge = Q4_MFMA_PREP_MIN_N_LARGE;
 // groups per wave when the A fragments of its range live in registers
 constexpr int kPrepMaxGroups = 5;
 // prepared fragments: per-row inverse scales (float) in the first 64 bytes
@@ -679,9 +687,11 @@ static int64_t frag_bytes(int64_t n, int64_t in) {
     return round256(kFragHeader + L.g4 * 4 * slots_for(n) * 64);
 }
 
-// Whether launches with n rows of x of width `in` use the pre-pass.
-static bool use_prep(int64_t n, int64_t in) {
-    return n >= kPrepMinN && frag_bytes(n, in) <= (int64_t)(kWorkspaceBytes / 4);
+// Whether a launch with n rows against an [out x in] matrix uses the pre-pass.
+static bool use_prep(int64_t n, int64_t out, int64_t in) {
+    if (frag_bytes(n, in) > (int64_t)(kWorkspaceBytes / 4)) return false;
+    if (n >= kPrepMinN) return true;
+    return n >= kPrepMinNLarge && Layout(out, in).tiles >= kMfmaManyTiles;
 }
 
 static int gpw_for(int64_t per, int64_t n, bool prep) {
@@ -692,7 +702,7 @@ static int gpw_for(int64_t per, int64_t n, bool prep) {
 
 static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     const Layout L(out, in);
-    const bool prep = use_prep(n, in);
+    const bool prep = use_prep(n, out, in);
     MfmaPlan p;
     // groups a wave may hold: the x it stages must fit its registers, or, when
     // prepared, the A fragments of its range
@@ -750,7 +760,7 @@ constexpr int64_t kMaxSlicedRows = 64;
 
 static size_t launch_workspace_bytes(int64_t n, int64_t out, int64_t in) {
     const size_t part = mfma_part_bytes(mfma_plan(n, out, in), out, in);
-    return part + (use_prep(n, in) ? (size_t)frag_bytes(n, in) : 0);
+    return part + (use_prep(n, out, in) ? (size_t)frag_bytes(n, in) : 0);
 }
 
 static size_t launch_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
@@ -793,6 +803,15 @@ bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     return launch_supported(kMaxRows, out, in) && launch_supported(tail_rows(n), out, in);
 }
 
+bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n) {
+    const int64_t rows[2] = {n < kMaxRows ? n : kMaxRows, tail_rows(n)};
+    for (int64_t r : rows)
+        for (int i = 1; i < count; ++i)
+            if (use_prep(r, probs[i].out, probs[i].in) != use_prep(r, probs[0].out, probs[0].in))
+                return false;
+    return true;
+}
+
 int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in) {
     const MfmaPlan p = mfma_plan(n, out, in);
     return p.gx * p.slices;
@@ -832,7 +851,8 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
     int waves = 1, gpw = 0;
     int64_t wg = 0, wsoff = 0;
     bool prep = true;
-    for (int i = 0; i < count; ++i) prep = prep && use_prep(NT, probs[i].in);
+    // the linears of a group agree on the pre-pass (gemv_mfma_group_uniform)
+    for (int i = 0; i < count; ++i) prep = prep && use_prep(NT, probs[i].out, probs[i].in);
     for (int i = 0; i < count; ++i) {
         const GemvProblem &pr = probs[i];
         const MfmaPlan p = mfma_plan(NT, pr.out, pr.in);

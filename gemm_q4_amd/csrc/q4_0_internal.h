@@ -49,6 +49,9 @@ struct GemvProblem {
 };
 bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16);
 size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in);
+// Whether one launch can carry these linears together: they agree on
+// converting x by a pre-pass for every row slice of an n-row call.
+bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n);
 int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y,
                             int64_t n, int64_t out, int64_t in, void *ws,

@@ -136,6 +136,29 @@ def test_grouped_ragged_shapes_shared_x_and_k_split(n):
         assert ratio(yy, blk, x, out, in_) <= TOL_SMALL_N
 
 
+@pytest.mark.parametrize("n", [4, 5, 6])
+def test_grouped_matrices_of_both_sizes(n):
+    """At 4 and 5 rows a matrix of 4096 tiles or more converts x by a pre-pass
+    and a small one does not, so such a group runs as separate launches; from
+    6 rows both use it and share one launch.  Every output as single calls
+    and within the small-n bound of the oracle."""
+    shapes = [(65536 + 40, 64), (96, 64), (65536, 96)]
+    xs = [synth.make_x(n, in_, seed=70 + i) for i, (_, in_) in enumerate(shapes)]
+    lins, blocks = [], []
+    for i, (out, in_) in enumerate(shapes):
+        blk = synth.make_blocks(out, in_, seed=80 + i)
+        p = packed_from_blocks(blk, out, in_)
+        lins.append((p, to_dev(xs[i]), torch.full((n, out), float("nan"), device=DEV), out, in_))
+        blocks.append(blk)
+    q4.q4_0_matmul_grouped(lins, q4.F32, n)
+    torch.cuda.synchronize()
+    for i, ((p, _, y, out, in_), blk) in enumerate(zip(lins, blocks)):
+        yy = y.cpu().numpy()
+        assert np.array_equal(yy, run(p, xs[i], out)), (out, in_)
+        rows = np.unique(np.linspace(0, out - 1, 64).astype(np.int64))
+        assert ratio(yy, blk, xs[i], out, in_, rows=rows) <= TOL_SMALL_N
+
+
 def test_grouped_prefill_runs_each_linear_with_the_gemm():
     n = 64
     x = synth.make_x(n, 256, seed=3, dtype=np.float16)
