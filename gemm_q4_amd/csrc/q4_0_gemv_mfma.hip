@@ -72,8 +72,13 @@ namespace q4 {
 #ifndef Q4_MFMA_MANY_TILES
 #define Q4_MFMA_MANY_TILES 4096
 #endif
+// LDS for a workgroup's staged A fragments; a K range whose fragments exceed
+// it is split.  Measured on MI355X: 96 KB keeps the block's 2560 x 9728 down
+// projection (76 groups) in one K slice at n = 2 and in two at n = 4
+// (grouped block n = 2/4: 29.0/35.8 us against 30.0/37.2 us with 56 KB);
+// 144 KB changes nothing measured.
 #ifndef Q4_MFMA_LDS_BUDGET
-#define Q4_MFMA_LDS_BUDGET (56 * 1024)
+#define Q4_MFMA_LDS_BUDGET (96 * 1024)
 #endif
 #ifndef Q4_MFMA_GROUPS_PER_WAVE
 #define Q4_MFMA_GROUPS_PER_WAVE 5
