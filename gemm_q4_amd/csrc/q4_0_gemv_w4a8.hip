@@ -40,7 +40,16 @@ namespace {
 constexpr int kW8MaxWaves = 8;
 constexpr int kW8MaxRows = 16;
 constexpr int kW8Groups = 5;          // groups a wave holds (A: 8 registers each)
+// Workgroups a launch aims for: about four per compute unit from
+// kW8ManyTiles tile-slices on, about one below (each workgroup walks a run
+// of tiles with its activation codes, as in the binary16 small-n kernel).
+#ifndef Q4_W8_TARGET_WGS_SMALL
+#define Q4_W8_TARGET_WGS_SMALL 256
+#endif
 constexpr int kW8TargetWgs = 1024;
+constexpr int kW8TargetWgsSmall = Q4_W8_TARGET_WGS_SMALL;
+constexpr int64_t kW8ManyTiles = 4096;
+constexpr int kW8ReduceBatch = 8;     // slice loads in flight per thread
 constexpr int kW8RedTiles = 2;
 
 typedef int i4_t __attribute__((ext_vector_type(4)));
@@ -251,9 +260,19 @@ __global__ __launch_bounds__(256) void w4a8_reduce_kernel(const float *__restric
         const int rr = (int)(e & 15);
         const int64_t tt = (e >> 4) % n;
         const int64_t t = (e >> 4) / n;
+        // the slices' loads in batches (indices past the last slice re-read
+        // it and are not added), added in slice order
         float s = 0.0f;
-        for (int64_t q = 0; q < slices; ++q)
-            s += part[((q * tiles + t) * kW8MaxRows + tt) * 16 + rr];
+        for (int64_t q0 = 0; q0 < slices; q0 += kW8ReduceBatch) {
+            float v[kW8ReduceBatch];
+#pragma unroll
+            for (int b = 0; b < kW8ReduceBatch; ++b) {
+                const int64_t q = q0 + b < slices ? q0 + b : slices - 1;
+                v[b] = part[((q * tiles + t) * kW8MaxRows + tt) * 16 + rr];
+            }
+#pragma unroll
+            for (int b = 0; b < kW8ReduceBatch; ++b) s += q0 + b < slices ? v[b] : 0.0f;
+        }
         const int64_t row = t * kTileRows + rr;
         if (row < out) y[tt * out + row] = s;
     }
@@ -274,7 +293,9 @@ W8Plan w8_plan(int64_t out, int64_t in) {
     if (waves < 1) waves = 1;
     p.per = (int)((p.gps + waves - 1) / waves);
     p.waves = (int)((p.gps + p.per - 1) / p.per);
-    int64_t tpw = (L.tiles * p.slices + kW8TargetWgs - 1) / kW8TargetWgs;
+    const int64_t units = L.tiles * p.slices;
+    const int64_t target = units >= kW8ManyTiles ? kW8TargetWgs : kW8TargetWgsSmall;
+    int64_t tpw = (units + target - 1) / target;
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
     p.gx = (L.tiles + tpw - 1) / tpw;
