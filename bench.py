@@ -305,7 +305,7 @@ def cpu_baseline(oracle, synth, out, in_, n, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only (--gpus must be 1); sharding is described, not run",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import torch
