@@ -387,11 +387,12 @@ def main():
                     extra["decode"].append(decode_line(torch, q4, synth, "logit_head",
                                                        [(151936, 2560)], nn, kernel, 200, 20,
                                                        argmax=True))
-            # the band between decode and prefill: the small-n kernel (16-row
-            # launches) against the tiled prefill product on the same shapes
+            # the band between decode and prefill: the small-n kernel (launches
+            # of up to 32 rows) against the tiled prefill product on the same
+            # shapes
             extra["mid_n"] = []
             up = [(9728, 2560)]
-            for nn in (16, 32):
+            for nn in (16, 32, 64):
                 for kk in (q4.KERNEL_AUTO, q4.KERNEL_GEMM):
                     extra["mid_n"].append(decode_line(torch, q4, synth, "ffn_up_decode", up, nn,
                                                       kk, 300, 20))

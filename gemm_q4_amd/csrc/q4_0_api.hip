@@ -65,9 +65,11 @@ bool supports(int kernel, int64_t n, int64_t out, int64_t in, int x_f16) {
 // Between decode and prefill (golem README, "Reading a prompt on the card":
 // mat-vec up to 16 columns, tiled products from 32): FFN-up 9728 x 2560 at
 // n = 9..16 runs in 11.1-11.7 us on the small-n kernel against 26.7-29.6 us
-// on the tiled product, and 16-row slices stay ahead up to n = 32 (23 us
-// against 32 us); at n = 48 the tiled product is ahead (33 us against 35).
-constexpr int64_t kSmallNMax = 32;
+// on the tiled product; with 32-row launches (two 16-row A groups sharing
+// each decoded weight fragment) n = 24/32 take 12.8/13.4 us against 32 us,
+// and two launches stay ahead up to the kernel's 64 rows (n = 40/48/64:
+// 23.4/24.6/26.9 us against 33.5/33.6/35.0 us).
+constexpr int64_t kSmallNMax = 64;
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (n <= kSmallNMax && q4::gemv_mfma_supports(n, out, in, x_f16))
         return Q4_0_KERNEL_GEMV_MFMA;

@@ -85,6 +85,7 @@ namespace q4 {
 #endif
 constexpr int kMfmaMaxWaves = 8;
 constexpr int kMaxRows = (int)kGemvLaunchRows;   // activation rows of one launch
+constexpr int kArgmaxRows = 16;                  // rows of one fused greedy-pick launch
 // rows <= 8: high and low binary16 part of each row (2n slots); 9..16 rows:
 // one binary16 slot per row
 template <int NT> constexpr bool split_rows() { return NT <= 8; }
@@ -111,10 +112,13 @@ constexpr int kMaxStageItems = 10;
 #endif
 constexpr int kPrepMinN = Q4_MFMA_PREP_MIN_N;
 constexpr int kPrepMinNLarge = Q4_MFMA_PREP_MIN_N_LARGE;
-// groups per wave when the A fragments of its range live in registers
+// groups per wave when the A fragments of its range live in registers (one
+// 16-row A group; two groups above 16 rows)
 constexpr int kPrepMaxGroups = 5;
-// prepared fragments: per-row inverse scales (float) in the first 64 bytes
-constexpr int kFragHeader = 64;
+constexpr int kPrepMaxGroups2 = 4;
+template <int NT> constexpr int prep_max_groups() { return NT > 16 ? kPrepMaxGroups2 : kPrepMaxGroups; }
+// prepared fragments: per-row inverse scales (float) in the first 128 bytes
+constexpr int kFragHeader = 128;
 // tiles whose per-wave partial sums are parked before a workgroup reduction
 // (16 KB of LDS whatever n is)
 template <int NT> constexpr int red_tiles() { return 32 / NT < 2 ? 2 : 32 / NT; }
@@ -351,11 +355,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     const int te = tb + a.tpw < a.tiles ? tb + a.tpw : a.tiles;
     const XT *__restrict__ x = (const XT *)a.x;
     const bool split = a.part != nullptr;
-    // running (max, index) of each row of y over this thread's outputs
-    float bv[NT];
-    int bi[NT];
+    // running (max, index) of each row of y over this thread's outputs (the
+    // fused greedy pick runs launches of at most kArgmaxRows rows)
+    constexpr int kAm = NT <= kArgmaxRows ? NT : 1;
+    float bv[kAm];
+    int bi[kAm];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < kAm; ++t) {
         bv[t] = -__builtin_huge_valf();
         bi[t] = 0x7fffffff;
     }
@@ -367,19 +373,28 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // stay finite).
     constexpr bool kSplit = split_rows<NT>();
     const int jslot = r < NT ? r : ((kSplit && r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
+    // above 16 rows a second A group holds rows 16 + r (prepared x only); each
+    // decoded weight fragment then feeds two products
+    constexpr int kRG = NT > 16 ? 2 : 1;
+    static_assert(kRG == 1 || PREP, "above 16 rows x is prepared");
+    const int jslot1 = 16 + r < NT ? 16 + r : 0;
     constexpr int kBlockFrag = row_slots<NT>() * 64;          // fragment bytes per block
     const int gw = ng > 0 ? gs0 + q0 : gs0;                   // first group of the wave
 
     // ---- prepared launch: request this lane's fragments ------------------------
     h8_t afr[PREP ? GPW : 1][4];
+    h8_t afr1[kRG == 2 ? GPW : 1][4];
     if constexpr (PREP) {
         const uint8_t *fb = a.frag + kFragHeader + (jslot * 4 + g) * 16;
+        const uint8_t *fb1 = a.frag + kFragHeader + (jslot1 * 4 + g) * 16;
 #pragma unroll
         for (int q = 0; q < GPW; ++q)
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
                 const int64_t b = (int64_t)(gw + (q < ng ? q : 0)) * 4 + s4;
                 afr[q][s4] = *reinterpret_cast<const h8_t *>(fb + b * kBlockFrag);
+                if constexpr (kRG == 2)
+                    afr1[q][s4] = *reinterpret_cast<const h8_t *>(fb1 + b * kBlockFrag);
             }
     }
 
@@ -483,12 +498,15 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // D slots a lane can hold live: 4g+i for i < min(NT, 4)
     constexpr int kLive = NT < 4 ? NT : 4;
     // inverse scale of the row behind D slot 4g+i (slot m and m+8 are one row)
-    float inv[kLive];
+    float inv[kLive], inv1[kLive];
 #pragma unroll
     for (int i = 0; i < kLive; ++i) {
         const int row = kSplit ? ((4 * g + i) & 7) : 4 * g + i;
+        inv1[i] = 1.0f;
         if constexpr (PREP) {
             inv[i] = row < NT ? reinterpret_cast<const float *>(a.frag)[row] : 1.0f;
+            if constexpr (kRG == 2)
+                inv1[i] = 16 + row < NT ? reinterpret_cast<const float *>(a.frag)[16 + row] : 1.0f;
         } else {
             float sc = 1.0f;
 #pragma unroll
@@ -503,14 +521,17 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // tile t + 1 are requested into the same registers as soon as group q of
     // tile t has consumed them.  The wave's sums are parked in red[slot].
     auto tile = [&](int t, int slot, bool next) {
-        float acc[kLive];
+        float acc[kLive], acc1[kLive];
 #pragma unroll
-        for (int k = 0; k < kLive; ++k) acc[k] = 0.0f;
+        for (int k = 0; k < kLive; ++k) {
+            acc[k] = 0.0f;
+            acc1[k] = 0.0f;
+        }
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (q < ng) {
                 const uint8_t *ag = afrag + q * 4 * kBlockFrag;
-                f4_t dd[4];
+                f4_t dd[4], dd1[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     h8_t av;
@@ -520,14 +541,20 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                         av = *reinterpret_cast<const h8_t *>(ag + s * kBlockFrag);
                     uint32_t qd[4];
                     decode_word_pairs(cw[q][s], mg, qd);
+                    const h8_t bw = pack_h8(qd);
                     const f4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    dd[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pack_h8(qd), z, 0, 0, 0);
+                    dd[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, z, 0, 0, 0);
+                    if constexpr (kRG == 2)
+                        dd1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr1[q][s], bw, z, 0, 0, 0);
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const float d = (float)as_h2(sw[q][s >> 1])[s & 1];   // v_fma_mix operand
 #pragma unroll
-                    for (int k = 0; k < kLive; ++k) acc[k] = __builtin_fmaf(d, dd[s][k], acc[k]);
+                    for (int k = 0; k < kLive; ++k) {
+                        acc[k] = __builtin_fmaf(d, dd[s][k], acc[k]);
+                        if constexpr (kRG == 2) acc1[k] = __builtin_fmaf(d, dd1[s][k], acc1[k]);
+                    }
                 }
             }
             if (next) load_group(t + 1, q);
@@ -545,6 +572,11 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             for (int i = 0; i < kLive; ++i)
                 if (4 * g + i < NT) red[slot][wave][4 * g + i][r] = v[i];
         }
+        if constexpr (kRG == 2) {
+#pragma unroll
+            for (int i = 0; i < kLive; ++i)
+                if (16 + 4 * g + i < NT) red[slot][wave][16 + 4 * g + i][r] = acc1[i] * inv1[i];
+        }
     };
 
     // Sum the parked partial sums of tiles [t0, t0 + cnt) over the waves, in
@@ -561,9 +593,11 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                 const int row = t * kTileRows + rr;
                 if (row < a.out) {
                     if (a.y) a.y[(int64_t)tt * a.out + row] = sum;
+                    if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
-                    for (int u = 0; u < NT; ++u)
-                        if (u == tt) amax_update(sum, row, bv[u], bi[u]);
+                        for (int u = 0; u < NT; ++u)
+                            if (u == tt) amax_update(sum, row, bv[u], bi[u]);
+                    }
                 }
             } else {
                 a.part[(((int64_t)sy * a.tiles + t) * kMaxRows + tt) * 16 + rr] = sum;
@@ -586,7 +620,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     }
     tile(t, t - t0, false);
     flush(t0, t - t0 + 1);
-    if (a.amax && !split) amax_workgroup<NT>(bv, bi, a.amax + (int64_t)local * NT);
+    if constexpr (NT <= kArgmaxRows)
+        if (a.amax && !split) amax_workgroup<NT>(bv, bi, a.amax + (int64_t)local * NT);
 }
 
 // Sum of the parked per-tile sums over the S slices, in slice order, for
@@ -608,10 +643,11 @@ constexpr int kReduceBatch = 8;   // slice loads in flight per thread
 template <int NT>
 __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs args) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    float bv[NT];
-    int bi[NT];
+    constexpr int kAm = NT <= kArgmaxRows ? NT : 1;
+    float bv[kAm];
+    int bi[kAm];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < kAm; ++t) {
         bv[t] = -__builtin_huge_valf();
         bi[t] = 0x7fffffff;
     }
@@ -641,12 +677,15 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
         const int64_t row = t * kTileRows + rr;
         if (row < L.out) {
             if (L.y) L.y[(int64_t)tt * L.out + row] = s;
+            if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
-            for (int u = 0; u < NT; ++u)
-                if (u == tt) amax_update(s, (int)row, bv[u], bi[u]);
+                for (int u = 0; u < NT; ++u)
+                    if (u == tt) amax_update(s, (int)row, bv[u], bi[u]);
+            }
         }
     }
-    if (args.amax) amax_workgroup<NT>(bv, bi, args.amax + (int64_t)blockIdx.x * NT);
+    if constexpr (NT <= kArgmaxRows)
+        if (args.amax) amax_workgroup<NT>(bv, bi, args.amax + (int64_t)blockIdx.x * NT);
 }
 
 // Final (max, index) of each row of y over `count` workgroup pairs; row t's
@@ -711,7 +750,8 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     MfmaPlan p;
     // groups a wave may hold: the x it stages must fit its registers, or, when
     // prepared, the A fragments of its range
-    int64_t per_cap = prep ? kPrepMaxGroups : (kMaxStageItems * 64) / (16 * n);
+    int64_t per_cap = prep ? (n > 16 ? kPrepMaxGroups2 : kPrepMaxGroups)
+                           : (kMaxStageItems * 64) / (16 * n);
     if (per_cap > 16) per_cap = 16;
     if (per_cap < 1) per_cap = 1;     // n > 16: no plan can run (gemv_mfma_supports)
     // slices: as few as keep the slice within the waves' capacity and, when
@@ -776,6 +816,7 @@ static size_t launch_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) 
 
 static bool launch_supported(int64_t n, int64_t out, int64_t in) {
     if (n < 1 || n > kMaxRows) return false;
+    if (n > 16 && !use_prep(n, out, in)) return false;   // two A groups need prepared x
     const MfmaPlan p = mfma_plan(n, out, in);
     if (p.gpw == 0 || p.waves > kMfmaMaxWaves || p.slices > 65535) return false;
     if ((int64_t)p.waves * p.per < p.gps) return false;
@@ -795,9 +836,11 @@ size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in) {
 }
 
 size_t gemv_mfma_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
-    if (n <= kMaxRows) return launch_argmax_workspace_bytes(n, out, in);
-    const size_t a = launch_argmax_workspace_bytes(kMaxRows, out, in);
-    const size_t b = launch_argmax_workspace_bytes(tail_rows(n), out, in);
+    // greedy-pick calls run as launches of up to kArgmaxRows rows
+    if (n <= kArgmaxRows) return launch_argmax_workspace_bytes(n, out, in);
+    const int64_t tail = n % kArgmaxRows == 0 ? kArgmaxRows : n % kArgmaxRows;
+    const size_t a = launch_argmax_workspace_bytes(kArgmaxRows, out, in);
+    const size_t b = launch_argmax_workspace_bytes(tail, out, in);
     return a > b ? a : b;
 }
 
@@ -822,35 +865,41 @@ int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in) {
     return p.gx * p.slices;
 }
 
+// Launches the instance if it exists (its groups fit the registers); returns
+// whether it did.
 template <int NT, typename XT, int GPW, bool PREP>
-static void launch_mfma_g(dim3 gd, dim3 bd, size_t lds, hipStream_t stream, const GemvArgs &a) {
-    if constexpr (PREP ? GPW <= kPrepMaxGroups
-                       : ((int64_t)GPW * 16 * NT + 63) / 64 <= kMaxStageItems)
+static bool launch_mfma_g(dim3 gd, dim3 bd, size_t lds, hipStream_t stream, const GemvArgs &a) {
+    if constexpr (PREP ? GPW <= prep_max_groups<NT>()
+                       : (NT <= 16 && ((int64_t)GPW * 16 * NT + 63) / 64 <= kMaxStageItems)) {
         hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW, PREP>), gd, bd, lds, stream, a);
+        return true;
+    }
+    return false;
 }
 
 template <int NT, typename XT, bool PREP>
 static hipError_t launch_mfma_p(int gpw, dim3 gd, dim3 bd, size_t lds, hipStream_t stream,
                                 const GemvArgs &a) {
+    bool launched = false;
     switch (gpw) {
-    case 1: launch_mfma_g<NT, XT, 1, PREP>(gd, bd, lds, stream, a); break;
-    case 2: launch_mfma_g<NT, XT, 2, PREP>(gd, bd, lds, stream, a); break;
-    case 4: launch_mfma_g<NT, XT, 4, PREP>(gd, bd, lds, stream, a); break;
-    case 5: launch_mfma_g<NT, XT, 5, PREP>(gd, bd, lds, stream, a); break;
-    case 8: if (PREP) return hipErrorInvalidValue;
-            launch_mfma_g<NT, XT, 8, PREP>(gd, bd, lds, stream, a); break;
-    case 10: if (PREP) return hipErrorInvalidValue;
-             launch_mfma_g<NT, XT, 10, PREP>(gd, bd, lds, stream, a); break;
-    case 16: if (PREP) return hipErrorInvalidValue;
-             launch_mfma_g<NT, XT, 16, PREP>(gd, bd, lds, stream, a); break;
-    default: return hipErrorInvalidValue;
+    case 1: launched = launch_mfma_g<NT, XT, 1, PREP>(gd, bd, lds, stream, a); break;
+    case 2: launched = launch_mfma_g<NT, XT, 2, PREP>(gd, bd, lds, stream, a); break;
+    case 4: launched = launch_mfma_g<NT, XT, 4, PREP>(gd, bd, lds, stream, a); break;
+    case 5: launched = launch_mfma_g<NT, XT, 5, PREP>(gd, bd, lds, stream, a); break;
+    case 8: if (!PREP) launched = launch_mfma_g<NT, XT, 8, PREP>(gd, bd, lds, stream, a); break;
+    case 10: if (!PREP) launched = launch_mfma_g<NT, XT, 10, PREP>(gd, bd, lds, stream, a); break;
+    case 16: if (!PREP) launched = launch_mfma_g<NT, XT, 16, PREP>(gd, bd, lds, stream, a); break;
+    default: break;
     }
+    if (!launched) return hipErrorInvalidValue;   // the plan asked for no compiled instance
     return hipGetLastError();
 }
 
 template <int NT, typename XT>
 static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
                                 hipStream_t stream, float *max_val, int32_t *max_idx) {
+    // the fused greedy pick runs launches of at most kArgmaxRows rows
+    if (NT > kArgmaxRows && max_val) return hipErrorInvalidValue;
     GemvArgs a = {};
     ReduceArgs ra = {};
     int waves = 1, gpw = 0;
@@ -936,8 +985,13 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         }
     }
     const dim3 gd((unsigned)wg), bd(waves * 64);
-    hipError_t e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
-                        : launch_mfma_p<NT, XT, false>(gpw, gd, bd, (size_t)lds, stream, a);
+    hipError_t e;
+    if constexpr (NT > 16)
+        e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
+                 : hipErrorInvalidValue;
+    else
+        e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
+                 : launch_mfma_p<NT, XT, false>(gpw, gd, bd, (size_t)lds, stream, a);
     if (e != hipSuccess) return e;
     if (ra.nlin > 0) {
         hipLaunchKernelGGL((gemv_mfma_reduce_kernel<NT>),
@@ -946,9 +1000,12 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         if (e != hipSuccess) return e;
     }
     if (!max_val) return hipSuccess;
-    hipLaunchKernelGGL((amax_final_kernel<NT>), dim3(1), dim3(256), 0, stream,
-                       (const uint2 *)pairs, npairs, max_val, max_idx);
-    return hipGetLastError();
+    if constexpr (NT <= kArgmaxRows) {
+        hipLaunchKernelGGL((amax_final_kernel<NT>), dim3(1), dim3(256), 0, stream,
+                           (const uint2 *)pairs, npairs, max_val, max_idx);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename XT>
@@ -971,6 +1028,22 @@ static hipError_t launch_mfma_x(const GemvProblem *probs, int count, int64_t n, 
     case 14: return launch_mfma_t<14, XT>(probs, count, ws, stream, mv, mi);
     case 15: return launch_mfma_t<15, XT>(probs, count, ws, stream, mv, mi);
     case 16: return launch_mfma_t<16, XT>(probs, count, ws, stream, mv, mi);
+    case 17: return launch_mfma_t<17, XT>(probs, count, ws, stream, mv, mi);
+    case 18: return launch_mfma_t<18, XT>(probs, count, ws, stream, mv, mi);
+    case 19: return launch_mfma_t<19, XT>(probs, count, ws, stream, mv, mi);
+    case 20: return launch_mfma_t<20, XT>(probs, count, ws, stream, mv, mi);
+    case 21: return launch_mfma_t<21, XT>(probs, count, ws, stream, mv, mi);
+    case 22: return launch_mfma_t<22, XT>(probs, count, ws, stream, mv, mi);
+    case 23: return launch_mfma_t<23, XT>(probs, count, ws, stream, mv, mi);
+    case 24: return launch_mfma_t<24, XT>(probs, count, ws, stream, mv, mi);
+    case 25: return launch_mfma_t<25, XT>(probs, count, ws, stream, mv, mi);
+    case 26: return launch_mfma_t<26, XT>(probs, count, ws, stream, mv, mi);
+    case 27: return launch_mfma_t<27, XT>(probs, count, ws, stream, mv, mi);
+    case 28: return launch_mfma_t<28, XT>(probs, count, ws, stream, mv, mi);
+    case 29: return launch_mfma_t<29, XT>(probs, count, ws, stream, mv, mi);
+    case 30: return launch_mfma_t<30, XT>(probs, count, ws, stream, mv, mi);
+    case 31: return launch_mfma_t<31, XT>(probs, count, ws, stream, mv, mi);
+    case 32: return launch_mfma_t<32, XT>(probs, count, ws, stream, mv, mi);
     default: return hipErrorInvalidValue;
     }
 }
@@ -986,8 +1059,8 @@ hipError_t launch_gemv_mfma_argmax(const void *packed, const void *x, int x_f16,
                                    int64_t n, int64_t out, int64_t in, float *max_val,
                                    int32_t *max_idx, void *ws, hipStream_t stream) {
     const int64_t esize = x_f16 ? 2 : 4;
-    for (int64_t r0 = 0; r0 < n; r0 += kMaxRows) {
-        const int64_t nr = n - r0 < kMaxRows ? n - r0 : kMaxRows;
+    for (int64_t r0 = 0; r0 < n; r0 += kArgmaxRows) {
+        const int64_t nr = n - r0 < kArgmaxRows ? n - r0 : kArgmaxRows;
         const GemvProblem p = {packed, (const uint8_t *)x + r0 * in * esize,
                                y ? y + r0 * out : nullptr, out, in};
         const hipError_t e =

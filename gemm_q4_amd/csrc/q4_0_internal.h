@@ -40,7 +40,7 @@ hipError_t launch_gemv_dpp(const void *packed, const void *x, int x_f16, float *
 // another (each linear's share is gemv_mfma_workspace_bytes).
 constexpr int kMaxGroupLinears = 8;
 // rows of x one small-n launch carries; more rows run as row slices
-constexpr int64_t kGemvLaunchRows = 16;
+constexpr int64_t kGemvLaunchRows = 32;
 struct GemvProblem {
     const void *packed;
     const void *x;

@@ -64,8 +64,8 @@ extern "C" {
                                    reduction; n <= 8                          */
 #define Q4_0_KERNEL_GEMV_MFMA 2 /* small n: fp16 MFMA; n <= 8: activations
                                    split into high and low binary16 parts;
-                                   9..16: one binary16 part; 17..64: 16-row
-                                   slices, one launch each                    */
+                                   9..32: one binary16 part per row, one
+                                   launch; 33..64: 32-row slices              */
 #define Q4_0_KERNEL_GEMM 3      /* prefill: 128 x 128 tiles, weights decoded
                                    to binary16, MFMA                          */
 
@@ -153,9 +153,9 @@ typedef struct q4_0_linear {
  *   No y may overlap any x, any packed W or another y of the group
  *   (Q4_0_EALIAS).  The x of different linears may be the same buffer.
  * When q4_0_matmul would run the small-n MFMA kernel on every linear
- * (n <= 32 for the usual shapes) the group runs as one launch per 16 rows
- * (plus the activation pre-pass from 4 rows, and a reduction launch if a
- * linear splits K); otherwise each linear runs as q4_0_matmul would, in array
+ * (n <= 64 for the usual shapes) the group runs as one launch per 32 rows
+ * (plus the activation pre-pass from 6 rows, or from 4 for matrices of 4096
+ * tiles or more, and a reduction launch if a linear splits K); otherwise each linear runs as q4_0_matmul would, in array
  * order.  Results equal those of q4_0_matmul on each linear alone. */
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream);

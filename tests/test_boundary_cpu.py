@@ -137,10 +137,13 @@ def test_kernel_choice_table():
             assert sel(n, out, in_) in (q4.KERNEL_GEMV_DPP, q4.KERNEL_GEMV_MFMA)
     assert sel(512, 9728, 2560, q4.F16) == q4.KERNEL_GEMM
     assert sel(512, 2560, 9728, q4.F16) == q4.KERNEL_GEMM
-    # the band between decode and prefill: small-n MFMA kernel up to 32 rows
+    # the band between decode and prefill: small-n MFMA kernel up to 64 rows
+    # (one launch up to 32, two above), the tiled product from 65
     assert sel(9, 100, 64) == q4.KERNEL_GEMV_MFMA
     assert sel(32, 9728, 2560) == q4.KERNEL_GEMV_MFMA
-    assert sel(33, 9728, 2560) == q4.KERNEL_GEMM
+    assert sel(33, 9728, 2560) == q4.KERNEL_GEMV_MFMA
+    assert sel(64, 9728, 2560) == q4.KERNEL_GEMV_MFMA
+    assert sel(65, 9728, 2560) == q4.KERNEL_GEMM
     with pytest.raises(q4.Q4Error):
         sel(0, 10, 64)
     with pytest.raises(q4.Q4Error):
