@@ -1,5 +1,6 @@
-// Small-n Q4_0 product on the matrix cores: y[n x out] = x . W^T for n <= 16,
-// for one linear or for a group of linears that share n in one launch.
+// Small-n Q4_0 product on the matrix cores: y[n x out] = x . W^T for n <= 32
+// rows per launch, for one linear or for a group of linears that share n in
+// one launch.
 //
 // Why MFMA for a memory-bound product: a vector-ALU dot costs about n + 1.25
 // VALU operations per weight, more than the ~3.9 per weight that 70% of HBM
@@ -23,9 +24,11 @@
 //   D: lane l holds slots 4*(l/16)+i, i = 0..3, of weight row l%16; per block
 //      acc += d * D in float32 (d is the row's binary16 scale).
 // hi and lo slots of a row are summed with one cross-lane shuffle (xor 32).
-// From 9 to 16 rows (the band between decode and prefill) each row takes one
-// slot holding its scaled binary16 value, without a low part: the precision
-// of the prefill kernel, which rounds x to binary16 as well (2^-11 relative).
+// From 9 rows (the band between decode and prefill) each row takes one slot
+// holding its scaled binary16 value, without a low part: the precision of the
+// prefill kernel, which rounds x to binary16 as well (2^-11 relative).  Above
+// 16 rows a second A operand holds rows 16..31 and each decoded B fragment
+// feeds both products, so the weights are still read once.
 //
 // Work split.  A workgroup owns a run of 16-row tiles of one linear and one
 // of its S slices of K; its waves take contiguous runs of `per` <= GPW
