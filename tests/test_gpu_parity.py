@@ -317,7 +317,7 @@ def test_mid_n_ffn_up_full_size_sampled_rows(n):
 
 def test_mid_n_grouped_and_argmax():
     shapes = [(4096, 2560), (1024, 2560), (1024, 2560)]
-    for n in (12, 20):                  # one grouped launch; row slices per linear
+    for n in (12, 20):    # one grouped launch (two A groups at 20 rows); the pick in 16-row launches
         x = synth.make_x(n, 2560, seed=n)
         xd = to_dev(x)
         lins, blocks = [], []
