@@ -427,6 +427,10 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     __builtin_amdgcn_s_barrier();
 
     // ---- epilogue ------------------------------------------------------------
+    // The tile's stores are non-temporal: written once, never read again by
+    // this kernel, and issued by all compute units at about the same time
+    // (measured in alternating runs: FFN-up 512 x 2560 . (9728 x 2560)^T
+    // 42.2-42.8 us against 43.4-43.8 us, FFN-down 39.4-39.7 against 39.7-40.0).
     // The K half wk = 1 writes its sums into a row-major tile in LDS (row
     // stride 136 floats: the two row groups of a write instruction land in
     // disjoint banks); wk = 0 reads them all, adds its own and writes the
@@ -474,8 +478,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
         for (int it = 0; it < kGemmBM * kGemmBN / 4 / (kGemmWaves * 64); ++it) {
             const int e = it * kGemmWaves * 64 + tid;          // float4 index in the tile
             const int row = e >> 5, col = (e & 31) * 4;
-            *reinterpret_cast<float4 *>(dst + row * kGemmBN + col) =
-                *reinterpret_cast<const float4 *>(ttile + row * kTileStride + col);
+            __builtin_nontemporal_store(*reinterpret_cast<const f4_t *>(ttile + row * kTileStride + col),
+                                        reinterpret_cast<f4_t *>(dst + row * kGemmBN + col));
         }
         return;
     }
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
         const float4 v = *reinterpret_cast<const float4 *>(ttile + row * kTileStride + col);
         float *yp = a.y + (int64_t)(m0 + row) * a.out + n0 + col;
         if (full_cols) {
-            *reinterpret_cast<float4 *>(yp) = v;
+            __builtin_nontemporal_store(__builtin_bit_cast(f4_t, v), reinterpret_cast<f4_t *>(yp));
         } else {
             const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
