@@ -230,3 +230,17 @@ def test_mfma_loop_validation():
     assert status_of(f, A16, 65537, 1, 0) == q4.EINVAL
     assert status_of(f, A16, 1, 0, 0) == q4.EINVAL
     assert status_of(f, A16, 1, 1000001, 0) == q4.EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; --gpus above 1 exits with a message
+    (status 2) before touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus_requested"] == 2 and "one GPU" in msg["error"]
