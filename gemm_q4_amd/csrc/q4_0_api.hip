@@ -290,10 +290,11 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
         const int wst = get_workspace(s, &ws);
         if (wst != Q4_0_OK) return wst;
     }
-    // one launch per slice of up to kGemvLaunchRows rows of every x and y
+    // one launch per slice of up to `lr` rows of every x and y
     const int64_t esize = elem_bytes(x_dtype);
-    for (int64_t r0 = 0; r0 < n; r0 += q4::kGemvLaunchRows) {
-        const int64_t nr = n - r0 < q4::kGemvLaunchRows ? n - r0 : q4::kGemvLaunchRows;
+    const int64_t lr = q4::gemv_mfma_launch_rows(probs, count);
+    for (int64_t r0 = 0; r0 < n; r0 += lr) {
+        const int64_t nr = n - r0 < lr ? n - r0 : lr;
         q4::GemvProblem ps[Q4_0_MAX_GROUP];
         for (int i = 0; i < count; ++i)
             ps[i] = {probs[i].packed, (const uint8_t *)probs[i].x + r0 * probs[i].in * esize,

@@ -93,7 +93,13 @@ constexpr int kArgmaxRows = 16;                  // rows of one fused greedy-pic
 // one binary16 slot per row
 template <int NT> constexpr bool split_rows() { return NT <= 8; }
 template <int NT> constexpr int row_slots() { return NT <= 8 ? 2 * NT : NT; }
-static int64_t slots_for(int64_t n) { return n <= 8 ? 2 * n : n; }
+// Kernel instance for a launch of n rows: exact up to 32 rows, then 48 or 64
+// rows with the launch's own row count bounding what is read and stored.
+constexpr int64_t kernel_rows(int64_t n) { return n <= 32 ? n : (n <= 48 ? 48 : 64); }
+static int64_t slots_for(int64_t n) {
+    n = kernel_rows(n);
+    return n <= 8 ? 2 * n : n;
+}
 constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
 constexpr int kMfmaTargetWgsSmall = Q4_MFMA_TARGET_WGS_SMALL;
 constexpr int64_t kMfmaManyTiles = Q4_MFMA_MANY_TILES;
@@ -118,13 +124,17 @@ constexpr int kPrepMinNLarge = Q4_MFMA_PREP_MIN_N_LARGE;
 // groups per wave when the A fragments of its range live in registers (one
 // 16-row A group; two groups above 16 rows)
 constexpr int kPrepMaxGroups = 5;
-constexpr int kPrepMaxGroups2 = 4;
-template <int NT> constexpr int prep_max_groups() { return NT > 16 ? kPrepMaxGroups2 : kPrepMaxGroups; }
-// prepared fragments: per-row inverse scales (float) in the first 128 bytes
-constexpr int kFragHeader = 128;
+constexpr int kPrepMaxGroups2 = 4;    // two A groups (17..32 rows)
+constexpr int kPrepMaxGroups4 = 2;    // three or four A groups (33..64 rows)
+constexpr int prep_groups(int64_t rows) {
+    return rows > 32 ? kPrepMaxGroups4 : (rows > 16 ? kPrepMaxGroups2 : kPrepMaxGroups);
+}
+template <int NT> constexpr int prep_max_groups() { return prep_groups(NT); }
+// prepared fragments: per-row inverse scales (float) in the first 256 bytes
+constexpr int kFragHeader = 256;
 // tiles whose per-wave partial sums are parked before a workgroup reduction
 // (16 KB of LDS whatever n is)
-template <int NT> constexpr int red_tiles() { return 32 / NT < 2 ? 2 : 32 / NT; }
+template <int NT> constexpr int red_tiles() { return NT > 32 ? 1 : (32 / NT < 2 ? 2 : 32 / NT); }
 // groups per wave a kernel instance holds in registers
 constexpr int kGpwSet[] = {1, 2, 4, 5, 8, 10, 16};
 
@@ -166,6 +176,7 @@ struct GemvLinear {
 struct GemvArgs {
     GemvLinear lin[kMaxGroupLinears];
     int nlin;
+    int nrows;            // activation rows of the launch (<= the instance's NT)
 };
 
 struct MfmaPlan {
@@ -376,28 +387,34 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // stay finite).
     constexpr bool kSplit = split_rows<NT>();
     const int jslot = r < NT ? r : ((kSplit && r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
-    // above 16 rows a second A group holds rows 16 + r (prepared x only); each
-    // decoded weight fragment then feeds two products
-    constexpr int kRG = NT > 16 ? 2 : 1;
+    // above 16 rows further A groups hold rows 16 j + r, j = 1 .. kRG - 1
+    // (prepared x only); each decoded weight fragment then feeds kRG products
+    constexpr int kRG = (NT + 15) / 16;
+    constexpr int kXG = kRG > 1 ? kRG - 1 : 1;               // array extent of the extra groups
     static_assert(kRG == 1 || PREP, "above 16 rows x is prepared");
-    const int jslot1 = 16 + r < NT ? 16 + r : 0;
+    int jslot_x[kXG];
+#pragma unroll
+    for (int j = 0; j < kXG; ++j) jslot_x[j] = 16 * (j + 1) + r < NT ? 16 * (j + 1) + r : 0;
     constexpr int kBlockFrag = row_slots<NT>() * 64;          // fragment bytes per block
     const int gw = ng > 0 ? gs0 + q0 : gs0;                   // first group of the wave
 
     // ---- prepared launch: request this lane's fragments ------------------------
     h8_t afr[PREP ? GPW : 1][4];
-    h8_t afr1[kRG == 2 ? GPW : 1][4];
+    h8_t afr_x[kXG][kRG > 1 ? GPW : 1][4];
     if constexpr (PREP) {
         const uint8_t *fb = a.frag + kFragHeader + (jslot * 4 + g) * 16;
-        const uint8_t *fb1 = a.frag + kFragHeader + (jslot1 * 4 + g) * 16;
 #pragma unroll
         for (int q = 0; q < GPW; ++q)
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
                 const int64_t b = (int64_t)(gw + (q < ng ? q : 0)) * 4 + s4;
                 afr[q][s4] = *reinterpret_cast<const h8_t *>(fb + b * kBlockFrag);
-                if constexpr (kRG == 2)
-                    afr1[q][s4] = *reinterpret_cast<const h8_t *>(fb1 + b * kBlockFrag);
+                if constexpr (kRG > 1) {
+#pragma unroll
+                    for (int j = 0; j < kRG - 1; ++j)
+                        afr_x[j][q][s4] = *reinterpret_cast<const h8_t *>(
+                            a.frag + kFragHeader + (jslot_x[j] * 4 + g) * 16 + b * kBlockFrag);
+                }
             }
     }
 
@@ -501,15 +518,21 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // D slots a lane can hold live: 4g+i for i < min(NT, 4)
     constexpr int kLive = NT < 4 ? NT : 4;
     // inverse scale of the row behind D slot 4g+i (slot m and m+8 are one row)
-    float inv[kLive], inv1[kLive];
+    float inv[kLive], inv_x[kXG][kLive];
 #pragma unroll
     for (int i = 0; i < kLive; ++i) {
         const int row = kSplit ? ((4 * g + i) & 7) : 4 * g + i;
-        inv1[i] = 1.0f;
+#pragma unroll
+        for (int j = 0; j < kXG; ++j) inv_x[j][i] = 1.0f;
         if constexpr (PREP) {
             inv[i] = row < NT ? reinterpret_cast<const float *>(a.frag)[row] : 1.0f;
-            if constexpr (kRG == 2)
-                inv1[i] = 16 + row < NT ? reinterpret_cast<const float *>(a.frag)[16 + row] : 1.0f;
+            if constexpr (kRG > 1) {
+#pragma unroll
+                for (int j = 0; j < kRG - 1; ++j) {
+                    const int rj = 16 * (j + 1) + row;
+                    inv_x[j][i] = rj < NT ? reinterpret_cast<const float *>(a.frag)[rj] : 1.0f;
+                }
+            }
         } else {
             float sc = 1.0f;
 #pragma unroll
@@ -524,17 +547,18 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // tile t + 1 are requested into the same registers as soon as group q of
     // tile t has consumed them.  The wave's sums are parked in red[slot].
     auto tile = [&](int t, int slot, bool next) {
-        float acc[kLive], acc1[kLive];
+        float acc[kLive], acc_x[kXG][kLive];
 #pragma unroll
         for (int k = 0; k < kLive; ++k) {
             acc[k] = 0.0f;
-            acc1[k] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kXG; ++j) acc_x[j][k] = 0.0f;
         }
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (q < ng) {
                 const uint8_t *ag = afrag + q * 4 * kBlockFrag;
-                f4_t dd[4], dd1[4];
+                f4_t dd[4], dd_x[kXG][4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     h8_t av;
@@ -547,8 +571,12 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                     const h8_t bw = pack_h8(qd);
                     const f4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
                     dd[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, z, 0, 0, 0);
-                    if constexpr (kRG == 2)
-                        dd1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr1[q][s], bw, z, 0, 0, 0);
+                    if constexpr (kRG > 1) {
+#pragma unroll
+                        for (int j = 0; j < kRG - 1; ++j)
+                            dd_x[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr_x[j][q][s], bw, z,
+                                                                                0, 0, 0);
+                    }
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -556,7 +584,11 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
 #pragma unroll
                     for (int k = 0; k < kLive; ++k) {
                         acc[k] = __builtin_fmaf(d, dd[s][k], acc[k]);
-                        if constexpr (kRG == 2) acc1[k] = __builtin_fmaf(d, dd1[s][k], acc1[k]);
+                        if constexpr (kRG > 1) {
+#pragma unroll
+                            for (int j = 0; j < kRG - 1; ++j)
+                                acc_x[j][k] = __builtin_fmaf(d, dd_x[j][s][k], acc_x[j][k]);
+                        }
                     }
                 }
             }
@@ -575,10 +607,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             for (int i = 0; i < kLive; ++i)
                 if (4 * g + i < NT) red[slot][wave][4 * g + i][r] = v[i];
         }
-        if constexpr (kRG == 2) {
+        if constexpr (kRG > 1) {
 #pragma unroll
-            for (int i = 0; i < kLive; ++i)
-                if (16 + 4 * g + i < NT) red[slot][wave][16 + 4 * g + i][r] = acc1[i] * inv1[i];
+            for (int j = 0; j < kRG - 1; ++j)
+#pragma unroll
+                for (int i = 0; i < kLive; ++i) {
+                    const int rj = 16 * (j + 1) + 4 * g + i;
+                    if (rj < NT) red[slot][wave][rj][r] = acc_x[j][i] * inv_x[j][i];
+                }
         }
     };
 
@@ -594,7 +630,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             for (int w = 0; w < nwaves; ++w) sum += red[sl][w][tt][rr];
             if (!split) {
                 const int row = t * kTileRows + rr;
-                if (row < a.out) {
+                if (row < a.out && tt < args.nrows) {
                     if (a.y) a.y[(int64_t)tt * a.out + row] = sum;
                     if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
@@ -638,6 +674,7 @@ struct ReduceLinear {
 struct ReduceArgs {
     ReduceLinear lin[kMaxGroupLinears];
     int nlin;
+    int nrows;           // activation rows of the launch
     int64_t total;
     uint2 *amax;         // per-workgroup (max, index) pairs of a single linear, or null
 };
@@ -678,7 +715,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
             for (int b = 0; b < kReduceBatch; ++b) s += q0 + b < L.slices ? v[b] : 0.0f;
         }
         const int64_t row = t * kTileRows + rr;
-        if (row < L.out) {
+        if (row < L.out && tt < args.nrows) {
             if (L.y) L.y[(int64_t)tt * L.out + row] = s;
             if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
@@ -750,11 +787,11 @@ static int gpw_for(int64_t per, int64_t n, bool prep) {
 static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     const Layout L(out, in);
     const bool prep = use_prep(n, out, in);
+    n = kernel_rows(n);
     MfmaPlan p;
     // groups a wave may hold: the x it stages must fit its registers, or, when
     // prepared, the A fragments of its range
-    int64_t per_cap = prep ? (n > 16 ? kPrepMaxGroups2 : kPrepMaxGroups)
-                           : (kMaxStageItems * 64) / (16 * n);
+    int64_t per_cap = prep ? prep_groups(n) : (kMaxStageItems * 64) / (16 * n);
     if (per_cap > 16) per_cap = 16;
     if (per_cap < 1) per_cap = 1;     // n > 16: no plan can run (gemv_mfma_supports)
     // slices: as few as keep the slice within the waves' capacity and, when
@@ -827,35 +864,73 @@ static bool launch_supported(int64_t n, int64_t out, int64_t in) {
     return launch_workspace_bytes(n, out, in) <= kWorkspaceBytes;
 }
 
-// The row counts of the slices of an n-row call: full kMaxRows slices and
-// the remainder (each slice's needs are those of its row count).
-static int64_t tail_rows(int64_t n) { return n % kMaxRows == 0 ? kMaxRows : n % kMaxRows; }
+// Rows per launch for one matrix: launches of up to 64 rows read the weights
+// once for all of them, but above 32 rows the K range is split (two groups
+// per wave) and the partial sums travel through the workspace.  Measured on
+// MI355X: FFN-up 9728 x 2560 at n = 48/64 22.4/25.9 us in one launch against
+// 24.9/27.0 us in 32-row launches, the block grouped at n = 64 104.9 against
+// 127.7 us; the 151936-row head at n = 64 237 us against 204 us.  So 64 rows
+// per launch below kMfmaManyTiles tiles, 32 from there on.
+static int64_t matrix_launch_rows(int64_t out, int64_t in) {
+    return Layout(out, in).tiles >= kMfmaManyTiles ? 32 : kMaxRows;
+}
+int64_t gemv_mfma_launch_rows(const GemvProblem *probs, int count) {
+    int64_t r = kMaxRows;
+    for (int i = 0; i < count; ++i) {
+        const int64_t ri = matrix_launch_rows(probs[i].out, probs[i].in);
+        if (ri < r) r = ri;
+    }
+    return r;
+}
 
+// The row counts of the slices of an n-row call in launches of `rows`:
+// full slices and the remainder (each slice's needs are those of its row
+// count).
+static int64_t tail_rows(int64_t n, int64_t rows) { return n % rows == 0 ? rows : n % rows; }
+
+static size_t sliced_workspace_bytes(int64_t n, int64_t rows, int64_t out, int64_t in) {
+    if (n <= rows) return launch_workspace_bytes(n, out, in);
+    const size_t a = launch_workspace_bytes(rows, out, in);
+    const size_t b = launch_workspace_bytes(tail_rows(n, rows), out, in);
+    return a > b ? a : b;
+}
+
+// Covers both launch heights, so a group that runs a small matrix in the
+// launches of a large one still fits.
 size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in) {
-    if (n <= kMaxRows) return launch_workspace_bytes(n, out, in);
-    const size_t a = launch_workspace_bytes(kMaxRows, out, in);
-    const size_t b = launch_workspace_bytes(tail_rows(n), out, in);
+    const size_t a = sliced_workspace_bytes(n, 32, out, in);
+    const size_t b = sliced_workspace_bytes(n, kMaxRows, out, in);
     return a > b ? a : b;
 }
 
 size_t gemv_mfma_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) {
     // greedy-pick calls run as launches of up to kArgmaxRows rows
     if (n <= kArgmaxRows) return launch_argmax_workspace_bytes(n, out, in);
-    const int64_t tail = n % kArgmaxRows == 0 ? kArgmaxRows : n % kArgmaxRows;
     const size_t a = launch_argmax_workspace_bytes(kArgmaxRows, out, in);
-    const size_t b = launch_argmax_workspace_bytes(tail, out, in);
+    const size_t b = launch_argmax_workspace_bytes(tail_rows(n, kArgmaxRows), out, in);
     return a > b ? a : b;
+}
+
+static bool sliced_supported(int64_t n, int64_t rows, int64_t out, int64_t in) {
+    if (n <= rows) return launch_supported(n, out, in);
+    return launch_supported(rows, out, in) && launch_supported(tail_rows(n, rows), out, in);
 }
 
 bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     (void)x_f16;
     if (n < 1 || n > kMaxSlicedRows) return false;
-    if (n <= kMaxRows) return launch_supported(n, out, in);
-    return launch_supported(kMaxRows, out, in) && launch_supported(tail_rows(n), out, in);
+    // both launch heights: a group may run this matrix in either
+    return sliced_supported(n, 32, out, in) && sliced_supported(n, kMaxRows, out, in);
 }
 
 bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n) {
-    const int64_t rows[2] = {n < kMaxRows ? n : kMaxRows, tail_rows(n)};
+    const int64_t lr = gemv_mfma_launch_rows(probs, count);
+    // row slices decide the precision of x (high and low parts up to 8 rows),
+    // so a group takes the slices each linear would take alone
+    if (n > 32)
+        for (int i = 0; i < count; ++i)
+            if (matrix_launch_rows(probs[i].out, probs[i].in) != lr) return false;
+    const int64_t rows[2] = {n < lr ? n : lr, tail_rows(n, lr)};
     for (int64_t r : rows)
         for (int i = 1; i < count; ++i)
             if (use_prep(r, probs[i].out, probs[i].in) != use_prep(r, probs[0].out, probs[0].in))
@@ -900,19 +975,22 @@ static hipError_t launch_mfma_p(int gpw, dim3 gd, dim3 bd, size_t lds, hipStream
 
 template <int NT, typename XT>
 static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
-                                hipStream_t stream, float *max_val, int32_t *max_idx) {
+                                hipStream_t stream, float *max_val, int32_t *max_idx,
+                                int64_t nrows) {
     // the fused greedy pick runs launches of at most kArgmaxRows rows
     if (NT > kArgmaxRows && max_val) return hipErrorInvalidValue;
     GemvArgs a = {};
     ReduceArgs ra = {};
+    a.nrows = (int)nrows;
+    ra.nrows = (int)nrows;
     int waves = 1, gpw = 0;
     int64_t wg = 0, wsoff = 0;
     bool prep = true;
     // the linears of a group agree on the pre-pass (gemv_mfma_group_uniform)
-    for (int i = 0; i < count; ++i) prep = prep && use_prep(NT, probs[i].out, probs[i].in);
+    for (int i = 0; i < count; ++i) prep = prep && use_prep(nrows, probs[i].out, probs[i].in);
     for (int i = 0; i < count; ++i) {
         const GemvProblem &pr = probs[i];
-        const MfmaPlan p = mfma_plan(NT, pr.out, pr.in);
+        const MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
         const Layout L(pr.out, pr.in);
         GemvLinear &g = a.lin[i];
         g.packed = (const uint8_t *)pr.packed;
@@ -958,10 +1036,12 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             if (a.lin[i].frag) continue;
             uint8_t *f = (uint8_t *)ws + wsoff;
             a.lin[i].frag = f;
-            wsoff += frag_bytes(NT, probs[i].in);
+            wsoff += frag_bytes(nrows, probs[i].in);
             const int nbpad = a.lin[i].g4 * 4;
-            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3(NT), dim3(kPrepThreads), 0, stream,
-                               (const XT *)probs[i].x, (int)probs[i].in, nbpad, f);
+            // one workgroup per row of x (rows of the instance past nrows are
+            // never read: their products land in outputs that are not stored)
+            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)nrows), dim3(kPrepThreads),
+                               0, stream, (const XT *)probs[i].x, (int)probs[i].in, nbpad, f);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1015,39 +1095,42 @@ template <typename XT>
 static hipError_t launch_mfma_x(const GemvProblem *probs, int count, int64_t n, void *ws,
                                 hipStream_t stream, float *mv, int32_t *mi) {
     switch (n) {
-    case 1: return launch_mfma_t<1, XT>(probs, count, ws, stream, mv, mi);
-    case 2: return launch_mfma_t<2, XT>(probs, count, ws, stream, mv, mi);
-    case 3: return launch_mfma_t<3, XT>(probs, count, ws, stream, mv, mi);
-    case 4: return launch_mfma_t<4, XT>(probs, count, ws, stream, mv, mi);
-    case 5: return launch_mfma_t<5, XT>(probs, count, ws, stream, mv, mi);
-    case 6: return launch_mfma_t<6, XT>(probs, count, ws, stream, mv, mi);
-    case 7: return launch_mfma_t<7, XT>(probs, count, ws, stream, mv, mi);
-    case 8: return launch_mfma_t<8, XT>(probs, count, ws, stream, mv, mi);
-    case 9: return launch_mfma_t<9, XT>(probs, count, ws, stream, mv, mi);
-    case 10: return launch_mfma_t<10, XT>(probs, count, ws, stream, mv, mi);
-    case 11: return launch_mfma_t<11, XT>(probs, count, ws, stream, mv, mi);
-    case 12: return launch_mfma_t<12, XT>(probs, count, ws, stream, mv, mi);
-    case 13: return launch_mfma_t<13, XT>(probs, count, ws, stream, mv, mi);
-    case 14: return launch_mfma_t<14, XT>(probs, count, ws, stream, mv, mi);
-    case 15: return launch_mfma_t<15, XT>(probs, count, ws, stream, mv, mi);
-    case 16: return launch_mfma_t<16, XT>(probs, count, ws, stream, mv, mi);
-    case 17: return launch_mfma_t<17, XT>(probs, count, ws, stream, mv, mi);
-    case 18: return launch_mfma_t<18, XT>(probs, count, ws, stream, mv, mi);
-    case 19: return launch_mfma_t<19, XT>(probs, count, ws, stream, mv, mi);
-    case 20: return launch_mfma_t<20, XT>(probs, count, ws, stream, mv, mi);
-    case 21: return launch_mfma_t<21, XT>(probs, count, ws, stream, mv, mi);
-    case 22: return launch_mfma_t<22, XT>(probs, count, ws, stream, mv, mi);
-    case 23: return launch_mfma_t<23, XT>(probs, count, ws, stream, mv, mi);
-    case 24: return launch_mfma_t<24, XT>(probs, count, ws, stream, mv, mi);
-    case 25: return launch_mfma_t<25, XT>(probs, count, ws, stream, mv, mi);
-    case 26: return launch_mfma_t<26, XT>(probs, count, ws, stream, mv, mi);
-    case 27: return launch_mfma_t<27, XT>(probs, count, ws, stream, mv, mi);
-    case 28: return launch_mfma_t<28, XT>(probs, count, ws, stream, mv, mi);
-    case 29: return launch_mfma_t<29, XT>(probs, count, ws, stream, mv, mi);
-    case 30: return launch_mfma_t<30, XT>(probs, count, ws, stream, mv, mi);
-    case 31: return launch_mfma_t<31, XT>(probs, count, ws, stream, mv, mi);
-    case 32: return launch_mfma_t<32, XT>(probs, count, ws, stream, mv, mi);
-    default: return hipErrorInvalidValue;
+    case 1: return launch_mfma_t<1, XT>(probs, count, ws, stream, mv, mi, n);
+    case 2: return launch_mfma_t<2, XT>(probs, count, ws, stream, mv, mi, n);
+    case 3: return launch_mfma_t<3, XT>(probs, count, ws, stream, mv, mi, n);
+    case 4: return launch_mfma_t<4, XT>(probs, count, ws, stream, mv, mi, n);
+    case 5: return launch_mfma_t<5, XT>(probs, count, ws, stream, mv, mi, n);
+    case 6: return launch_mfma_t<6, XT>(probs, count, ws, stream, mv, mi, n);
+    case 7: return launch_mfma_t<7, XT>(probs, count, ws, stream, mv, mi, n);
+    case 8: return launch_mfma_t<8, XT>(probs, count, ws, stream, mv, mi, n);
+    case 9: return launch_mfma_t<9, XT>(probs, count, ws, stream, mv, mi, n);
+    case 10: return launch_mfma_t<10, XT>(probs, count, ws, stream, mv, mi, n);
+    case 11: return launch_mfma_t<11, XT>(probs, count, ws, stream, mv, mi, n);
+    case 12: return launch_mfma_t<12, XT>(probs, count, ws, stream, mv, mi, n);
+    case 13: return launch_mfma_t<13, XT>(probs, count, ws, stream, mv, mi, n);
+    case 14: return launch_mfma_t<14, XT>(probs, count, ws, stream, mv, mi, n);
+    case 15: return launch_mfma_t<15, XT>(probs, count, ws, stream, mv, mi, n);
+    case 16: return launch_mfma_t<16, XT>(probs, count, ws, stream, mv, mi, n);
+    case 17: return launch_mfma_t<17, XT>(probs, count, ws, stream, mv, mi, n);
+    case 18: return launch_mfma_t<18, XT>(probs, count, ws, stream, mv, mi, n);
+    case 19: return launch_mfma_t<19, XT>(probs, count, ws, stream, mv, mi, n);
+    case 20: return launch_mfma_t<20, XT>(probs, count, ws, stream, mv, mi, n);
+    case 21: return launch_mfma_t<21, XT>(probs, count, ws, stream, mv, mi, n);
+    case 22: return launch_mfma_t<22, XT>(probs, count, ws, stream, mv, mi, n);
+    case 23: return launch_mfma_t<23, XT>(probs, count, ws, stream, mv, mi, n);
+    case 24: return launch_mfma_t<24, XT>(probs, count, ws, stream, mv, mi, n);
+    case 25: return launch_mfma_t<25, XT>(probs, count, ws, stream, mv, mi, n);
+    case 26: return launch_mfma_t<26, XT>(probs, count, ws, stream, mv, mi, n);
+    case 27: return launch_mfma_t<27, XT>(probs, count, ws, stream, mv, mi, n);
+    case 28: return launch_mfma_t<28, XT>(probs, count, ws, stream, mv, mi, n);
+    case 29: return launch_mfma_t<29, XT>(probs, count, ws, stream, mv, mi, n);
+    case 30: return launch_mfma_t<30, XT>(probs, count, ws, stream, mv, mi, n);
+    case 31: return launch_mfma_t<31, XT>(probs, count, ws, stream, mv, mi, n);
+    case 32: return launch_mfma_t<32, XT>(probs, count, ws, stream, mv, mi, n);
+    default:
+        if (n <= 48) return launch_mfma_t<48, XT>(probs, count, ws, stream, mv, mi, n);
+        if (n <= 64) return launch_mfma_t<64, XT>(probs, count, ws, stream, mv, mi, n);
+        return hipErrorInvalidValue;
     }
 }
 
@@ -1077,8 +1160,9 @@ hipError_t launch_gemv_mfma_argmax(const void *packed, const void *x, int x_f16,
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y, int64_t n,
                             int64_t out, int64_t in, void *ws, hipStream_t stream) {
     const int64_t esize = x_f16 ? 2 : 4;
-    for (int64_t r0 = 0; r0 < n; r0 += kMaxRows) {
-        const int64_t nr = n - r0 < kMaxRows ? n - r0 : kMaxRows;
+    const int64_t lr = matrix_launch_rows(out, in);
+    for (int64_t r0 = 0; r0 < n; r0 += lr) {
+        const int64_t nr = n - r0 < lr ? n - r0 : lr;
         const GemvProblem p = {packed, (const uint8_t *)x + r0 * in * esize, y + r0 * out, out,
                                in};
         const hipError_t e = launch_gemv_mfma_group(&p, 1, nr, x_f16, ws, stream);

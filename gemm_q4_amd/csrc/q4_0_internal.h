@@ -20,7 +20,7 @@ inline int64_t grid_for(int64_t total, int block) {
 // Workspace for kernels that split K across workgroups: per-slice partial
 // sums, written by the product kernel and read by the reduction kernel that
 // follows it on the same stream.
-constexpr size_t kWorkspaceBytes = size_t(32) << 20;
+constexpr size_t kWorkspaceBytes = size_t(128) << 20;
 
 hipError_t launch_repack(const void *blocks, void *packed, int64_t out, int64_t in,
                          hipStream_t stream);
@@ -40,7 +40,7 @@ hipError_t launch_gemv_dpp(const void *packed, const void *x, int x_f16, float *
 // another (each linear's share is gemv_mfma_workspace_bytes).
 constexpr int kMaxGroupLinears = 8;
 // rows of x one small-n launch carries; more rows run as row slices
-constexpr int64_t kGemvLaunchRows = 32;
+constexpr int64_t kGemvLaunchRows = 64;
 struct GemvProblem {
     const void *packed;
     const void *x;
@@ -49,8 +49,12 @@ struct GemvProblem {
 };
 bool gemv_mfma_supports(int64_t n, int64_t out, int64_t in, int x_f16);
 size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in);
-// Whether one launch can carry these linears together: they agree on
-// converting x by a pre-pass for every row slice of an n-row call.
+// Whether one launch can carry these linears together: they agree on the
+// rows per launch and on converting x by a pre-pass for every row slice of an
+// n-row call.
+// Rows per launch for a group of linears (32 or 64: the smallest any of
+// them takes alone).
+int64_t gemv_mfma_launch_rows(const GemvProblem *probs, int count);
 bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n);
 int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y,

@@ -20,9 +20,10 @@
  *    stream of the current device).  The current HIP device must be the one
  *    holding the buffers.
  *  - Device memory: some calls need a workspace: shapes whose K is split
- *    across workgroups (partial sums), and small-n calls with n >= 4 (the
- *    activations converted once into the matrix-core operand layout).
- *    q4_0_matmul allocates it (32 MiB, hipMalloc) the first time such a call
+ *    across workgroups (partial sums), and small-n calls from 6 rows, or
+ *    from 4 for matrices of 4096 16-row tiles or more (the activations
+ *    converted once into the matrix-core operand layout).
+ *    q4_0_matmul allocates it (128 MiB, hipMalloc) the first time such a call
  *    runs on a (device, stream) pair and keeps it for later calls on that
  *    pair until q4_0_release_workspaces.  Run one call per stream before
  *    capturing that stream into a graph.  Nothing else is allocated.
@@ -64,8 +65,9 @@ extern "C" {
                                    reduction; n <= 8                          */
 #define Q4_0_KERNEL_GEMV_MFMA 2 /* small n: fp16 MFMA; n <= 8: activations
                                    split into high and low binary16 parts;
-                                   9..32: one binary16 part per row, one
-                                   launch; 33..64: 32-row slices              */
+                                   9..64: one binary16 part per row; one
+                                   launch up to 64 rows (32 for matrices of
+                                   4096 tiles or more), row slices above      */
 #define Q4_0_KERNEL_GEMM 3      /* prefill: 128 x 128 tiles, weights decoded
                                    to binary16, MFMA                          */
 
@@ -153,7 +155,8 @@ typedef struct q4_0_linear {
  *   No y may overlap any x, any packed W or another y of the group
  *   (Q4_0_EALIAS).  The x of different linears may be the same buffer.
  * When q4_0_matmul would run the small-n MFMA kernel on every linear
- * (n <= 64 for the usual shapes) the group runs as one launch per 32 rows
+ * (n <= 64 for the usual shapes) the group runs as one launch per 64 rows (32
+ * when a matrix has 4096 tiles or more; above 32 rows the linears must agree)
  * (plus the activation pre-pass from 6 rows, or from 4 for matrices of 4096
  * tiles or more, and a reduction launch if a linear splits K); otherwise each linear runs as q4_0_matmul would, in array
  * order.  Results equal those of q4_0_matmul on each linear alone. */

@@ -136,12 +136,14 @@ def test_grouped_ragged_shapes_shared_x_and_k_split(n):
         assert ratio(yy, blk, x, out, in_) <= TOL_SMALL_N
 
 
-@pytest.mark.parametrize("n", [4, 5, 6])
+@pytest.mark.parametrize("n", [4, 5, 6, 40])
 def test_grouped_matrices_of_both_sizes(n):
     """At 4 and 5 rows a matrix of 4096 tiles or more converts x by a pre-pass
     and a small one does not, so such a group runs as separate launches; from
-    6 rows both use it and share one launch.  Every output as single calls
-    and within the small-n bound of the oracle."""
+    6 rows both use it and share one launch; at 40 rows the large matrices
+    take 32-row launches and the small one a 40-row launch, so the group runs
+    as separate launches again.  Every output as single calls and within the
+    small-n bound of the oracle."""
     shapes = [(65536 + 40, 64), (96, 64), (65536, 96)]
     xs = [synth.make_x(n, in_, seed=70 + i) for i, (_, in_) in enumerate(shapes)]
     lins, blocks = [], []
