@@ -155,11 +155,12 @@ typedef struct q4_0_linear {
  *   No y may overlap any x, any packed W or another y of the group
  *   (Q4_0_EALIAS).  The x of different linears may be the same buffer.
  * When q4_0_matmul would run the small-n MFMA kernel on every linear
- * (n <= 64 for the usual shapes) the group runs as one launch per 64 rows (32
- * when a matrix has 4096 tiles or more; above 32 rows the linears must agree)
- * (plus the activation pre-pass from 6 rows, or from 4 for matrices of 4096
- * tiles or more, and a reduction launch if a linear splits K); otherwise each linear runs as q4_0_matmul would, in array
- * order.  Results equal those of q4_0_matmul on each linear alone. */
+ * (n <= 64 for the usual shapes) the group runs as one launch per 64 rows
+ * (32 when a matrix has 4096 tiles or more; above 32 rows the linears must
+ * agree), plus the activation pre-pass from 6 rows (from 4 for matrices of
+ * 4096 tiles or more) and a reduction launch if a linear splits K; otherwise
+ * each linear runs as q4_0_matmul would, in array order.  Results equal those
+ * of q4_0_matmul on each linear alone. */
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream);
 
