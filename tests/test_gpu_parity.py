@@ -295,7 +295,9 @@ def test_runs_on_a_side_stream():
 BOUND_MID_N = 2.0 ** -11 * 1.01 + 1e-6
 
 
-@pytest.mark.parametrize("n", [9, 12, 16, 17, 31, 32, 40, 64])
+# 33..48 rows run the 48-row instance, 49..64 the 64-row one, with the
+# launch's own row count: 33, 40, 50 and 64 cover both and their edges
+@pytest.mark.parametrize("n", [9, 12, 16, 17, 31, 32, 33, 40, 50, 64])
 @pytest.mark.parametrize("out,in_", [(300, 160), (37, 4128)])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16], ids=["xf32", "xf16"])
 def test_mid_n_parity(n, out, in_, xdt):
@@ -306,7 +308,7 @@ def test_mid_n_parity(n, out, in_, xdt):
     assert r <= BOUND_MID_N and r <= TOL_GEMM, r
 
 
-@pytest.mark.parametrize("n", [12, 32])
+@pytest.mark.parametrize("n", [12, 32, 50])
 def test_mid_n_ffn_up_full_size_sampled_rows(n):
     out, in_ = 9728, 2560
     blk = synth.make_blocks(out, in_, seed=0)
