@@ -362,8 +362,11 @@ def main():
                "algorithmic_bytes_per_launch": per_launch_bytes,
                "timing": "HIP graph replay of the step's launches",
                "grouped": groups is not None, "argmax": args.argmax, "w4a8": args.w4a8,
-               "ms_per_step_eager": round(ms_eager, 6)}
-        dtype = "f32"
+               "ms_per_step_eager": round(ms_eager, 6),
+               # the products: binary16 operands (x as high and low parts up to
+               # 8 rows), float32 accumulation; W4A8: int8 operands, int32 sums
+               "accumulate": "i32 then f32" if args.w4a8 else "f32"}
+        dtype = "i8" if args.w4a8 else "f16"
         del cases
         torch.cuda.empty_cache()
         extra = {}

@@ -121,8 +121,8 @@ constexpr int kMaxStageItems = 10;
 #endif
 constexpr int kPrepMinN = Q4_MFMA_PREP_MIN_N;
 constexpr int kPrepMinNLarge = Q4_MFMA_PREP_MIN_N_LARGE;
-// groups per wave when the A fragments of its range live in registers (one
-// 16-row A group; two groups above 16 rows)
+// groups per wave when the A fragments of its range live in registers: 5 with
+// one 16-row A group, 4 with two, 2 with three or four
 constexpr int kPrepMaxGroups = 5;
 constexpr int kPrepMaxGroups2 = 4;    // two A groups (17..32 rows)
 constexpr int kPrepMaxGroups4 = 2;    // three or four A groups (33..64 rows)
