@@ -319,6 +319,20 @@ def test_mid_n_ffn_up_full_size_sampled_rows(n):
     assert ratio(y, blk, x, out, in_, rows=rows) <= BOUND_MID_N
 
 
+def test_mid_n_head_runs_in_32_row_launches():
+    """The 151936-row head (4096 tiles or more) takes 32-row launches above 32
+    rows: at 40 rows one launch of 32 and one of 8 (whose x is split into high
+    and low parts); sampled rows against the oracle within the mid-n bound."""
+    out, in_, n = 151936, 2560, 40
+    blk = synth.make_blocks(out, in_, seed=11)
+    x = synth.make_x(n, in_, seed=12)
+    assert q4.q4_0_select_kernel(n, out, in_) == q4.KERNEL_GEMV_MFMA
+    y = run(packed_from_blocks(blk, out, in_), x, out)
+    rows = np.unique(np.concatenate([[0, out - 1],
+                                     np.random.default_rng(3).integers(0, out, size=64)]))
+    assert ratio(y, blk, x, out, in_, rows=rows) <= BOUND_MID_N
+
+
 def test_mid_n_grouped_and_argmax():
     shapes = [(4096, 2560), (1024, 2560), (1024, 2560)]
     for n in (12, 20):    # one grouped launch (two A groups at 20 rows); the pick in 16-row launches
