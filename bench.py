@@ -121,7 +121,6 @@ def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None, argm
     replayed: the device runs the same kernels on the same buffers, without
     the Python and driver launch cost between them (how a decode loop would
     run them).  Returns (ms per step, steps actually timed)."""
-    stream = torch.cuda.current_stream()
     ncopy = len(cases[0].packed)
     for grp in groups or ():
         for k in grp:
@@ -158,6 +157,13 @@ def timed(torch, q4, cases, kernel, steps, warmup, graph=True, groups=None, argm
                 [(cases[k].packed[i % ncopy], xg, cases[k].y, cases[k].out, cases[k].in_)
                  for k in grp], cases[grp[0]].xcode, cases[grp[0]].n, sh)
 
+    return time_steps(torch, step, ncopy, steps, warmup, graph)
+
+
+def time_steps(torch, step, ncopy, steps, warmup, graph=True):
+    """Time step(i, stream) as `timed` describes (graph replay over `ncopy`
+    weight copies, or eager launches); return (ms per step, steps timed)."""
+    stream = torch.cuda.current_stream()
     for i in range(warmup):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
@@ -245,6 +251,56 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, group
            "grouped": groups is not None, "argmax": argmax, "w4a8": w4a8,
            "rotation_copies": copies}
     del cases
+    torch.cuda.empty_cache()
+    return res
+
+
+def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_=2048):
+    """Routed (mixture-of-experts) decode, synthetic: n rows of x, each through
+    k distinct experts drawn from n_exp experts of out x in (an expert FFN
+    projection of a mid-size mixture model; the experts' shape is chosen, not
+    taken from a page).  One q4_0_matmul_routed launch per step, against the
+    same pairs as n*k single-row q4_0_matmul calls.  GB/s counts the distinct
+    experts' Q4_0 bytes of a step."""
+    eb = q4.q4_0_blocks_bytes(out, in_)
+    pb = q4.q4_0_packed_bytes(out, in_)
+    copies = copies_for(n_exp * eb)
+    parts = []
+    for e in range(n_exp):
+        b = torch.from_numpy(synth.make_blocks(out, in_, seed=500 + e).reshape(-1)).cuda()
+        parts.append(q4.repacked(b, out, in_))
+    base = torch.cat(parts)
+    del parts
+    stacks = [base] + [base.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(synth.make_x(n, in_, seed=501)).cuda()
+    rng = np.random.default_rng(502)
+    route_np = np.stack([rng.permutation(n_exp)[:k] for _ in range(n)]).astype(np.int32)
+    route = torch.from_numpy(route_np).cuda()
+    y = torch.empty((n * k, out), dtype=torch.float32, device="cuda")
+    uniq = len(np.unique(route_np))
+
+    def routed(i, sh):
+        q4.q4_0_matmul_routed(stacks[i % copies], n_exp, x, q4.F32, route, k, y, n, out, in_,
+                              sh)
+
+    def singles(i, sh):
+        st = stacks[i % copies]
+        for t in range(n):
+            for j in range(k):
+                e, p = int(route_np[t, j]), t * k + j
+                q4.q4_0_matmul_ex(st[e * pb:(e + 1) * pb], x[t:t + 1], q4.F32, y[p:p + 1], 1,
+                                  out, in_, q4.KERNEL_GEMV_MFMA, sh)
+
+    ms, done = time_steps(torch, routed, copies, steps, warmup)
+    ms_single, _ = time_steps(torch, singles, copies, steps, warmup)
+    gbs = uniq * eb / (ms * 1e-3) / 1e9
+    res = {"workload": "moe_routed_decode", "n": n, "experts": n_exp, "k": k,
+           "expert_shape": [out, in_], "distinct_experts": uniq,
+           "ms_per_step": round(ms, 5), "steps": done,
+           "ms_per_step_single_calls": round(ms_single, 5),
+           "weight_bytes": uniq * eb, "GB/s": round(gbs, 1),
+           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "rotation_copies": copies}
+    del stacks, base
     torch.cuda.empty_cache()
     return res
 
@@ -408,6 +464,7 @@ def main():
                 decode_line(torch, q4, synth, "block_decode", blk, 4, 0, 200, 20, w4a8=True),
                 decode_line(torch, q4, synth, "logit_head", [(151936, 2560)], 1, 0, 200, 20,
                             w4a8=True)]
+            extra["routed"] = [routed_line(torch, q4, synth, nn, 300, 20) for nn in (1, 4)]
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
 
     if args.calib_copy:

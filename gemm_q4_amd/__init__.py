@@ -61,6 +61,7 @@ KERNEL_AUTO, KERNEL_GEMV_DPP, KERNEL_GEMV_MFMA, KERNEL_GEMM = 0, 1, 2, 3
 KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GEMV_DPP: "gemv_dpp",
                 KERNEL_GEMV_MFMA: "gemv_mfma", KERNEL_GEMM: "gemm"}
 MAX_IN, MAX_OUT, MAX_N = 1048576, 16777216, 65536
+MAX_EXPERTS, MAX_ROUTED = 4096, 64
 
 _i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
@@ -80,6 +81,7 @@ _SIGS = {
     "q4_0_quantize_x8": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _vp]),
     "q4_0_matmul_w4a8": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4_0_mfma_loop": (_int, [_vp, _i64, _i64, ctypes.POINTER(_i64), _vp]),
+    "q4_0_matmul_routed": (_int, [_vp, _i64, _vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -227,6 +229,19 @@ def matmul_w4a8(packed, q, d, out: int, y=None, stream=None):
     return y
 
 
+def matmul_routed(experts, n_experts: int, x, route, out: int, y=None, stream=None):
+    """y[t*k + j] = x[t] . W_{route[t, j]}^T for a stack of repacked experts
+    (one flat uint8 tensor, n_experts matrices of q4_0_packed_bytes apart) and
+    route an int32 [n x k] device tensor.  Returns y [n*k x out]."""
+    import torch
+    n, in_ = x.shape
+    k = route.shape[1]
+    if y is None:
+        y = torch.empty((n * k, out), dtype=torch.float32, device=x.device)
+    q4_0_matmul_routed(experts, n_experts, x, dtype_code(x), route, k, y, n, out, in_, stream)
+    return y
+
+
 def q4_0_select_kernel(n: int, out: int, in_: int, x_dtype: int = F32) -> int:
     return _check(_lib.q4_0_select_kernel(n, out, in_, x_dtype), "q4_0_select_kernel")
 
@@ -238,6 +253,13 @@ def q4_0_kernel_supports(kernel: int, n: int, out: int, in_: int,
         return False
     _check(st, "q4_0_kernel_supports")
     return True
+
+
+def q4_0_matmul_routed(experts, n_experts: int, x, x_dtype: int, route, k: int, y, n: int,
+                       out: int, in_: int, stream=None) -> None:
+    _check(_lib.q4_0_matmul_routed(_ptr(experts), n_experts, _ptr(x), x_dtype, _ptr(route), k,
+                                   _ptr(y), n, out, in_, _stream(stream, y, x)),
+           "q4_0_matmul_routed")
 
 
 def q4_0_mfma_loop(sink, workgroups: int, iters: int, stream=None) -> int:

@@ -243,6 +243,35 @@ int q4_0_matmul_w4a8(const void *packed, const int8_t *q, const float *d, float 
     return map_hip(q4::launch_gemv_w4a8(packed, q, d, y, n, out, in, ws, s));
 }
 
+int q4_0_matmul_routed(const void *experts, int64_t n_experts, const void *x, int x_dtype,
+                       const int32_t *route, int64_t k, float *y, int64_t n, int64_t out,
+                       int64_t in, void *stream) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    if (n_experts < 1 || n_experts > Q4_0_MAX_EXPERTS || k < 1 || k > Q4_0_MAX_ROUTED)
+        return Q4_0_EINVAL;
+    if (!experts || !x || !route || !y) return Q4_0_ENULL;
+    if (!aligned(experts, 16) || !aligned(x, 16) || !aligned(route, 4) || !aligned(y, 4))
+        return Q4_0_EALIGN;
+    const int64_t pairs = n * k;
+    const size_t ybytes = (size_t)pairs * (size_t)out * 4u;
+    const size_t xbytes = (size_t)n * (size_t)in * (size_t)elem_bytes(x_dtype);
+    const size_t wbytes = (size_t)n_experts * q4_0_packed_bytes(out, in);
+    if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, experts, wbytes) ||
+        overlaps(y, ybytes, route, (size_t)pairs * 4u))
+        return Q4_0_EALIAS;
+    if (!q4::gemv_mfma_routed_supports(pairs, out, in)) return Q4_0_EUNSUPPORTED;
+    const hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (q4::gemv_mfma_routed_workspace_bytes(pairs, out, in) > 0) {
+        const int wst = get_workspace(s, &ws);
+        if (wst != Q4_0_OK) return wst;
+    }
+    return map_hip(q4::launch_gemv_mfma_routed(experts, n_experts, x, x_dtype == Q4_0_F16,
+                                               route, k, y, n, out, in, ws, s));
+}
+
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream) {
     if (!linears) return Q4_0_ENULL;

@@ -173,10 +173,24 @@ struct GemvLinear {
     int wg0;             // first workgroup of this linear in the launch
 };
 
+// A routed launch (mixture of experts, by column): lin[0] describes the
+// geometry of every expert; pair p = column * k + slot computes row p of y
+// from x row p / k and the expert route[p] of a stack of experts.
+struct GemvRoute {
+    const int32_t *route; // device, one expert index per pair; null: not routed
+    int64_t expert_bytes; // bytes from one expert's packed matrix to the next
+    int64_t x_row_bytes;  // bytes from one x row to the next
+    int64_t part_pair;    // floats of partial sums per pair (K split), else 0
+    int n_experts;
+    int k;                // pairs per x row
+    int wpp;              // workgroups per pair
+};
+
 struct GemvArgs {
     GemvLinear lin[kMaxGroupLinears];
     int nlin;
     int nrows;            // activation rows of the launch (<= the instance's NT)
+    GemvRoute rt;
 };
 
 struct MfmaPlan {
@@ -356,8 +370,22 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     int li = 0;
     for (int k = 1; k < args.nlin; ++k)
         if ((int)blockIdx.x >= args.lin[k].wg0) li = k;
-    const GemvLinear &a = args.lin[li];
-    const int local = (int)blockIdx.x - a.wg0;
+    GemvLinear a = args.lin[li];
+    int local = (int)blockIdx.x - a.wg0;
+    // routed launch: this pair's expert, x row, y row and partial sums; an
+    // expert index outside the stack reads expert 0 and stores NaN
+    bool bad_route = false;
+    if (args.rt.route) {
+        const int pair = (int)blockIdx.x / args.rt.wpp;
+        local = (int)blockIdx.x - pair * args.rt.wpp;
+        int e = __builtin_amdgcn_readfirstlane(args.rt.route[pair]);
+        bad_route = e < 0 || e >= args.rt.n_experts;
+        if (bad_route) e = 0;
+        a.packed += (int64_t)e * args.rt.expert_bytes;
+        a.x = (const uint8_t *)a.x + (int64_t)(pair / args.rt.k) * args.rt.x_row_bytes;
+        a.y += (int64_t)pair * a.out;
+        if (a.part) a.part += (int64_t)pair * args.rt.part_pair;
+    }
     const int sy = local / a.gx;                              // K slice
     const int cx = local - sy * a.gx;
     const int gs0 = sy * a.gps;                               // first group of the slice
@@ -631,6 +659,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             if (!split) {
                 const int row = t * kTileRows + rr;
                 if (row < a.out && tt < args.nrows) {
+                    if (bad_route) sum = __builtin_nanf("");
                     if (a.y) a.y[(int64_t)tt * a.out + row] = sum;
                     if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
@@ -639,7 +668,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                     }
                 }
             } else {
-                a.part[(((int64_t)sy * a.tiles + t) * kMaxRows + tt) * 16 + rr] = sum;
+                a.part[(((int64_t)sy * a.tiles + t) * kMaxRows + tt) * 16 + rr] =
+                    bad_route ? __builtin_nanf("") : sum;
             }
         }
         __syncthreads();
@@ -675,6 +705,10 @@ struct ReduceArgs {
     ReduceLinear lin[kMaxGroupLinears];
     int nlin;
     int nrows;           // activation rows of the launch
+    // routed launch: lin[0] per pair, pair_elems flat elements each, its
+    // partial sums part_pair floats and its y row out floats further on
+    int64_t pair_elems;
+    int64_t part_pair;
     int64_t total;
     uint2 *amax;         // per-workgroup (max, index) pairs of a single linear, or null
 };
@@ -696,8 +730,14 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
         int li = 0;
         for (int k = 1; k < args.nlin; ++k)
             if (f >= args.lin[k].e0) li = k;
-        const ReduceLinear &L = args.lin[li];
-        const int64_t e = f - L.e0;
+        ReduceLinear L = args.lin[li];
+        int64_t e = f - L.e0;
+        if (args.pair_elems > 0) {                   // routed: pair of element f
+            const int64_t pair = e / args.pair_elems;
+            e -= pair * args.pair_elems;
+            L.part += pair * args.part_pair;
+            L.y += pair * L.out;
+        }
         const int rr = (int)(e & 15);
         const int tt = (int)((e >> 4) % NT);
         const int64_t t = (e >> 4) / NT;
@@ -976,9 +1016,12 @@ static hipError_t launch_mfma_p(int gpw, dim3 gd, dim3 bd, size_t lds, hipStream
 template <int NT, typename XT>
 static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
                                 hipStream_t stream, float *max_val, int32_t *max_idx,
-                                int64_t nrows) {
+                                int64_t nrows, const GemvRoute *route = nullptr,
+                                int64_t npairs_routed = 0) {
     // the fused greedy pick runs launches of at most kArgmaxRows rows
     if (NT > kArgmaxRows && max_val) return hipErrorInvalidValue;
+    // a routed launch: one linear (the experts' geometry), no pick
+    if (route && (count != 1 || max_val || npairs_routed < 1)) return hipErrorInvalidValue;
     GemvArgs a = {};
     ReduceArgs ra = {};
     a.nrows = (int)nrows;
@@ -1009,7 +1052,15 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             rl.slices = p.slices;
             rl.e0 = ra.total;
             ra.total += L.tiles * NT * 16;
-            wsoff += (int64_t)mfma_part_bytes(p, pr.out, pr.in);
+            const int64_t pb = (int64_t)mfma_part_bytes(p, pr.out, pr.in);
+            if (route) {                            // each pair its own partial sums
+                ra.pair_elems = L.tiles * NT * 16;
+                ra.part_pair = pb / (int64_t)sizeof(float);
+                ra.total = ra.pair_elems * npairs_routed;
+                wsoff += pb * npairs_routed;
+            } else {
+                wsoff += pb;
+            }
         }
         g.code_base = L.scale_bytes();
         g.out = (int)pr.out;
@@ -1026,6 +1077,12 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         if (p.gpw > gpw) gpw = p.gpw;
     }
     a.nlin = count;
+    if (route) {
+        a.rt = *route;
+        a.rt.wpp = (int)wg;                         // the one linear's workgroups
+        a.rt.part_pair = ra.part_pair;
+        wg *= npairs_routed;
+    }
     // prepared launch: one pre-pass per distinct x of the group, its
     // fragments after the partial sums in the workspace
     if (prep) {
@@ -1169,6 +1226,34 @@ hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Routed (mixture of experts, by column): every (x row, expert) pair is a
+// one-row product of its own, all pairs in one launch.
+size_t gemv_mfma_routed_workspace_bytes(int64_t pairs, int64_t out, int64_t in) {
+    return (size_t)pairs * mfma_part_bytes(mfma_plan(1, out, in), out, in);
+}
+
+bool gemv_mfma_routed_supports(int64_t pairs, int64_t out, int64_t in) {
+    if (pairs < 1 || !launch_supported(1, out, in)) return false;
+    const MfmaPlan p = mfma_plan(1, out, in);
+    return p.gx * p.slices * pairs <= 0x7fffffff &&
+           gemv_mfma_routed_workspace_bytes(pairs, out, in) <= kWorkspaceBytes;
+}
+
+hipError_t launch_gemv_mfma_routed(const void *experts, int64_t n_experts, const void *x,
+                                   int x_f16, const int32_t *route, int64_t k, float *y,
+                                   int64_t n, int64_t out, int64_t in, void *ws,
+                                   hipStream_t stream) {
+    GemvRoute rt = {};
+    rt.route = route;
+    rt.expert_bytes = Layout(out, in).total_bytes();
+    rt.x_row_bytes = in * (x_f16 ? 2 : 4);
+    rt.n_experts = (int)n_experts;
+    rt.k = (int)k;
+    const GemvProblem p = {experts, x, y, out, in};
+    return x_f16 ? launch_mfma_t<1, _Float16>(&p, 1, ws, stream, nullptr, nullptr, 1, &rt, n * k)
+                 : launch_mfma_t<1, float>(&p, 1, ws, stream, nullptr, nullptr, 1, &rt, n * k);
 }
 
 }  // namespace q4

@@ -56,6 +56,15 @@ size_t gemv_mfma_workspace_bytes(int64_t n, int64_t out, int64_t in);
 // them takes alone).
 int64_t gemv_mfma_launch_rows(const GemvProblem *probs, int count);
 bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n);
+// Routed small-n product (mixture of experts, by column): y row p = x row
+// p / k times the transpose of expert route[p] of a stack of n_experts
+// repacked [out x in] matrices; every pair in one launch.
+bool gemv_mfma_routed_supports(int64_t pairs, int64_t out, int64_t in);
+size_t gemv_mfma_routed_workspace_bytes(int64_t pairs, int64_t out, int64_t in);
+hipError_t launch_gemv_mfma_routed(const void *experts, int64_t n_experts, const void *x,
+                                   int x_f16, const int32_t *route, int64_t k, float *y,
+                                   int64_t n, int64_t out, int64_t in, void *ws,
+                                   hipStream_t stream);
 int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y,
                             int64_t n, int64_t out, int64_t in, void *ws,

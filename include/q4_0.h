@@ -164,6 +164,28 @@ typedef struct q4_0_linear {
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,
                         void *stream);
 
+/* Mixture-of-experts product, by column (golem-server README, "On the card":
+ * a column reads the matrices it was routed to, and the by-column kernels
+ * take a column offset so that one pass answers several columns):
+ *     y[t*k + j][o] = sum_i W_e[o][i] * x[t][i],   e = route[t*k + j],
+ * for every column t < n and slot j < k, all n*k pairs in one launch of the
+ * small-n MFMA kernel (one row each, with the precision of q4_0_matmul at
+ * n = 1).
+ *   experts : DEVICE, n_experts repacked [out x in] matrices back to back,
+ *             q4_0_packed_bytes(out, in) bytes apart, 16-byte aligned;
+ *   x       : DEVICE [n x in] (x_dtype); route : DEVICE int32 [n x k];
+ *   y       : DEVICE float32 [n*k x out], overwritten, overlapping neither
+ *             x, the experts nor route (Q4_0_EALIAS).
+ * 1 <= n_experts <= Q4_0_MAX_EXPERTS, 1 <= k <= Q4_0_MAX_ROUTED.  The routing
+ * stays on the device (no host round trip); an index outside [0, n_experts)
+ * reads expert 0 and makes that pair's row NaN.  Q4_0_EUNSUPPORTED when the
+ * pairs' K-split partial sums would not fit the stream's workspace. */
+#define Q4_0_MAX_EXPERTS 4096
+#define Q4_0_MAX_ROUTED 64
+int q4_0_matmul_routed(const void *experts, int64_t n_experts, const void *x, int x_dtype,
+                       const int32_t *route, int64_t k, float *y, int64_t n, int64_t out,
+                       int64_t in, void *stream);
+
 /* Logit-head product with its epilogue fused: y = x . W^T as in
  * q4_0_matmul (small-n kernel, n <= 8), and for every row t of y its largest
  * value max_val[t] and that value's index max_idx[t] (the smallest index

@@ -244,3 +244,22 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus_requested"] == 2 and "one GPU" in msg["error"]
+
+
+def test_routed_validation():
+    f = q4.q4_0_matmul_routed
+    D16 = 1 << 38
+    E16 = 1 << 39
+    # experts, n_experts, x, x_dtype, route, k, y, n, out, in
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, D16, 1, 10, 48, 0) == q4.ESHAPE
+    assert status_of(f, A16, 0, B16, q4.F32, C16, 2, D16, 1, 10, 64, 0) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 0, D16, 1, 10, 64, 0) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, C16, q4.MAX_ROUTED + 1, D16, 1, 10, 64, 0) == q4.EINVAL
+    assert status_of(f, A16, q4.MAX_EXPERTS + 1, B16, q4.F32, C16, 2, D16, 1, 10, 64, 0) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, 7, C16, 2, D16, 1, 10, 64, 0) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, 0, 2, D16, 1, 10, 64, 0) == q4.ENULL
+    assert status_of(f, A16 + 8, 4, B16, q4.F32, C16, 2, D16, 1, 10, 64, 0) == q4.EALIGN
+    assert status_of(f, A16, 4, B16, q4.F32, C16 + 2, 2, D16, 1, 10, 64, 0) == q4.EALIGN
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, B16 + 16, 1, 10, 64, 0) == q4.EALIAS
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, A16 + 64, 1, 10, 64, 0) == q4.EALIAS
+    assert status_of(f, A16, 4, B16, q4.F32, E16, 2, E16 - 64, 1, 10, 64, 0) == q4.EALIAS

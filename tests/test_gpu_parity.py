@@ -625,3 +625,59 @@ def test_mfma_loop_aid_checksums_and_flops():
         want[lane] = 8 * iters * D[rows, c].sum()
     got = sink.cpu().numpy().reshape(wgs * 4, 64)
     assert np.array_equal(got, np.broadcast_to(want, got.shape).astype(np.float32))
+
+
+# ------------------------------------------------------------------ routed (by column)
+def _expert_stack(n_experts, out, in_, seed):
+    blks = [synth.make_blocks(out, in_, seed=seed + e) for e in range(n_experts)]
+    stack = torch.cat([packed_from_blocks(b, out, in_).reshape(-1) for b in blks])
+    return blks, stack
+
+
+@pytest.mark.parametrize("n,k,out,in_", [(1, 8, 300, 160), (3, 4, 37, 4128),
+                                         (2, 3, 64, 9728)])    # the last one K-split
+@pytest.mark.parametrize("xdt", [np.float32, np.float16], ids=["xf32", "xf16"])
+def test_routed_equals_single_calls_and_oracle(n, k, out, in_, xdt):
+    """Every (row, expert) pair of a routed launch equals the one-row product
+    with that expert bit for bit, and matches the oracle."""
+    n_exp = 6
+    blks, stack = _expert_stack(n_exp, out, in_, seed=70)
+    x = synth.make_x(n, in_, seed=71, dtype=xdt)
+    route = np.random.default_rng(72).integers(0, n_exp, size=(n, k)).astype(np.int32)
+    y = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out)
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    pb = q4.q4_0_packed_bytes(out, in_)
+    for t in range(n):
+        for j in range(k):
+            p, e = t * k + j, int(route[t, j])
+            single = run(stack[e * pb:(e + 1) * pb], x[t:t + 1], out, kernel=q4.KERNEL_GEMV_MFMA)
+            assert np.array_equal(yy[p:p + 1], single), (t, j, e)
+            assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_) <= TOL_SMALL_N
+
+
+def test_routed_index_outside_the_stack_gives_nan_rows():
+    out, in_, n_exp = 100, 4128, 3        # K-split: NaN passes through the reduction
+    blks, stack = _expert_stack(n_exp, out, in_, seed=80)
+    x = synth.make_x(2, in_, seed=81)
+    route = np.array([[0, -1], [n_exp, 2]], dtype=np.int32)
+    yy = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out).cpu().numpy()
+    assert np.isnan(yy[1]).all() and np.isnan(yy[2]).all()
+    assert ratio(yy[0:1], blks[0], x[0:1], out, in_) <= TOL_SMALL_N
+    assert ratio(yy[3:4], blks[2], x[1:2], out, in_) <= TOL_SMALL_N
+
+
+def test_routed_moe_full_size_sampled_rows():
+    """A synthetic mixture-of-experts up projection: 128 experts of 768 x 2048,
+    8 experts per row, 4 rows; sampled output rows against the oracle."""
+    out, in_, n_exp, k, n = 768, 2048, 128, 8, 4
+    blks, stack = _expert_stack(n_exp, out, in_, seed=90)
+    x = synth.make_x(n, in_, seed=91)
+    rng = np.random.default_rng(92)
+    route = np.stack([rng.permutation(n_exp)[:k] for _ in range(n)]).astype(np.int32)
+    yy = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out).cpu().numpy()
+    rows = np.arange(3, out, 11)
+    for t in range(n):
+        for j in range(k):
+            p, e = t * k + j, int(route[t, j])
+            assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_, rows=rows) <= TOL_SMALL_N
