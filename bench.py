@@ -259,9 +259,10 @@ def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_
     """Routed (mixture-of-experts) decode, synthetic: n rows of x, each through
     k distinct experts drawn from n_exp experts of out x in (an expert FFN
     projection of a mid-size mixture model; the experts' shape is chosen, not
-    taken from a page).  One q4_0_matmul_routed launch per step, against the
-    same pairs as n*k single-row q4_0_matmul calls.  GB/s counts the distinct
-    experts' Q4_0 bytes of a step."""
+    taken from a page).  One q4_0_matmul_routed call per step, timed by
+    column, by expert and as AUTO picks, and for n <= 4 against the same pairs
+    as n*k single-row q4_0_matmul calls.  GB/s counts the distinct experts'
+    Q4_0 bytes of a step."""
     eb = q4.q4_0_blocks_bytes(out, in_)
     pb = q4.q4_0_packed_bytes(out, in_)
     copies = copies_for(n_exp * eb)
@@ -279,9 +280,11 @@ def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_
     y = torch.empty((n * k, out), dtype=torch.float32, device="cuda")
     uniq = len(np.unique(route_np))
 
-    def routed(i, sh):
-        q4.q4_0_matmul_routed(stacks[i % copies], n_exp, x, q4.F32, route, k, y, n, out, in_,
-                              sh)
+    def routed(rk):
+        def step(i, sh):
+            q4.q4_0_matmul_routed_ex(stacks[i % copies], n_exp, x, q4.F32, route, k, y, n, out,
+                                     in_, rk, sh)
+        return step
 
     def singles(i, sh):
         st = stacks[i % copies]
@@ -291,15 +294,25 @@ def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_
                 q4.q4_0_matmul_ex(st[e * pb:(e + 1) * pb], x[t:t + 1], q4.F32, y[p:p + 1], 1,
                                   out, in_, q4.KERNEL_GEMV_MFMA, sh)
 
-    ms, done = time_steps(torch, routed, copies, steps, warmup)
-    ms_single, _ = time_steps(torch, singles, copies, steps, warmup)
-    gbs = uniq * eb / (ms * 1e-3) / 1e9
+    auto = q4.q4_0_select_route(n, k, n_exp, out, in_)
+    ms = {}
+    for name, rk in (("by_column", q4.ROUTE_BY_COLUMN), ("by_expert", q4.ROUTE_BY_EXPERT)):
+        try:
+            ms[name], done = time_steps(torch, routed(rk), copies, steps, warmup)
+        except q4.Q4Error:
+            ms[name] = None
+    best = ms["by_column" if auto == q4.ROUTE_BY_COLUMN else "by_expert"]
+    gbs = uniq * eb / (best * 1e-3) / 1e9
     res = {"workload": "moe_routed_decode", "n": n, "experts": n_exp, "k": k,
            "expert_shape": [out, in_], "distinct_experts": uniq,
-           "ms_per_step": round(ms, 5), "steps": done,
-           "ms_per_step_single_calls": round(ms_single, 5),
+           "auto": "by_column" if auto == q4.ROUTE_BY_COLUMN else "by_expert",
+           "ms_per_step": round(best, 5), "steps": done,
+           "ms_by_column": ms["by_column"] and round(ms["by_column"], 5),
+           "ms_by_expert": ms["by_expert"] and round(ms["by_expert"], 5),
            "weight_bytes": uniq * eb, "GB/s": round(gbs, 1),
            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "rotation_copies": copies}
+    if n <= 4:
+        res["ms_single_calls"] = round(time_steps(torch, singles, copies, steps, warmup)[0], 5)
     del stacks, base
     torch.cuda.empty_cache()
     return res
@@ -464,7 +477,8 @@ def main():
                 decode_line(torch, q4, synth, "block_decode", blk, 4, 0, 200, 20, w4a8=True),
                 decode_line(torch, q4, synth, "logit_head", [(151936, 2560)], 1, 0, 200, 20,
                             w4a8=True)]
-            extra["routed"] = [routed_line(torch, q4, synth, nn, 300, 20) for nn in (1, 4)]
+            extra["routed"] = [routed_line(torch, q4, synth, nn, 300, 20)
+                               for nn in (1, 4, 16, 64)]
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
 
     if args.calib_copy:

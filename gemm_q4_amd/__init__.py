@@ -62,6 +62,7 @@ KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GEMV_DPP: "gemv_dpp",
                 KERNEL_GEMV_MFMA: "gemv_mfma", KERNEL_GEMM: "gemm"}
 MAX_IN, MAX_OUT, MAX_N = 1048576, 16777216, 65536
 MAX_EXPERTS, MAX_ROUTED = 4096, 64
+ROUTE_AUTO, ROUTE_BY_COLUMN, ROUTE_BY_EXPERT = 0, 1, 2
 
 _i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
@@ -82,6 +83,9 @@ _SIGS = {
     "q4_0_matmul_w4a8": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4_0_mfma_loop": (_int, [_vp, _i64, _i64, ctypes.POINTER(_i64), _vp]),
     "q4_0_matmul_routed": (_int, [_vp, _i64, _vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
+    "q4_0_matmul_routed_ex": (_int, [_vp, _i64, _vp, _int, _vp, _i64, _vp, _i64, _i64, _i64,
+                                     _int, _vp]),
+    "q4_0_select_route": (_int, [_i64, _i64, _i64, _i64, _i64]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -229,7 +233,8 @@ def matmul_w4a8(packed, q, d, out: int, y=None, stream=None):
     return y
 
 
-def matmul_routed(experts, n_experts: int, x, route, out: int, y=None, stream=None):
+def matmul_routed(experts, n_experts: int, x, route, out: int, y=None, stream=None,
+                  route_kernel: int = ROUTE_AUTO):
     """y[t*k + j] = x[t] . W_{route[t, j]}^T for a stack of repacked experts
     (one flat uint8 tensor, n_experts matrices of q4_0_packed_bytes apart) and
     route an int32 [n x k] device tensor.  Returns y [n*k x out]."""
@@ -238,7 +243,8 @@ def matmul_routed(experts, n_experts: int, x, route, out: int, y=None, stream=No
     k = route.shape[1]
     if y is None:
         y = torch.empty((n * k, out), dtype=torch.float32, device=x.device)
-    q4_0_matmul_routed(experts, n_experts, x, dtype_code(x), route, k, y, n, out, in_, stream)
+    q4_0_matmul_routed_ex(experts, n_experts, x, dtype_code(x), route, k, y, n, out, in_,
+                          route_kernel, stream)
     return y
 
 
@@ -260,6 +266,17 @@ def q4_0_matmul_routed(experts, n_experts: int, x, x_dtype: int, route, k: int, 
     _check(_lib.q4_0_matmul_routed(_ptr(experts), n_experts, _ptr(x), x_dtype, _ptr(route), k,
                                    _ptr(y), n, out, in_, _stream(stream, y, x)),
            "q4_0_matmul_routed")
+
+
+def q4_0_matmul_routed_ex(experts, n_experts: int, x, x_dtype: int, route, k: int, y, n: int,
+                          out: int, in_: int, route_kernel: int, stream=None) -> None:
+    _check(_lib.q4_0_matmul_routed_ex(_ptr(experts), n_experts, _ptr(x), x_dtype, _ptr(route),
+                                      k, _ptr(y), n, out, in_, route_kernel,
+                                      _stream(stream, y, x)), "q4_0_matmul_routed_ex")
+
+
+def q4_0_select_route(n: int, k: int, n_experts: int, out: int, in_: int) -> int:
+    return _check(_lib.q4_0_select_route(n, k, n_experts, out, in_), "q4_0_select_route")
 
 
 def q4_0_mfma_loop(sink, workgroups: int, iters: int, stream=None) -> int:

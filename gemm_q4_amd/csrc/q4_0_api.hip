@@ -70,6 +70,14 @@ bool supports(int kernel, int64_t n, int64_t out, int64_t in, int x_f16) {
 // and two launches stay ahead up to the kernel's 64 rows (n = 40/48/64:
 // 23.4/24.6/26.9 us against 33.5/33.6/35.0 us).
 constexpr int64_t kSmallNMax = 64;
+// Routed products (golem-server README, "On the card": a column reads the
+// matrices it was routed to, a prompt reads each expert once for the columns
+// that chose it, the two crossing near thirty-two columns): by expert from
+// this many x rows, by column below.  Measured on MI355X (128 experts of 768 x
+// 2048, 8 per row, graph replay), by column against by expert: n = 1 4.7 /
+// 12.9 us, n = 8 15.4 / 30.9, n = 16 28.6 / 39.9, n = 32 49.5 / 47.6, n = 64
+// 89.9 / 54.2.
+constexpr int64_t kByExpertMinN = 32;
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (n <= kSmallNMax && q4::gemv_mfma_supports(n, out, in, x_f16))
         return Q4_0_KERNEL_GEMV_MFMA;
@@ -246,9 +254,31 @@ int q4_0_matmul_w4a8(const void *packed, const int8_t *q, const float *d, float 
 int q4_0_matmul_routed(const void *experts, int64_t n_experts, const void *x, int x_dtype,
                        const int32_t *route, int64_t k, float *y, int64_t n, int64_t out,
                        int64_t in, void *stream) {
+    return q4_0_matmul_routed_ex(experts, n_experts, x, x_dtype, route, k, y, n, out, in,
+                                 Q4_0_ROUTE_AUTO, stream);
+}
+
+int q4_0_select_route(int64_t n, int64_t k, int64_t n_experts, int64_t out, int64_t in) {
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (n_experts < 1 || n_experts > Q4_0_MAX_EXPERTS || k < 1 || k > Q4_0_MAX_ROUTED)
+        return Q4_0_EINVAL;
+    const bool col = q4::gemv_mfma_routed_supports(n * k, out, in);
+    const bool exp = q4::gemv_mfma_by_expert_supports(n * k, n_experts, out, in);
+    if (exp && (n >= kByExpertMinN || !col)) return Q4_0_ROUTE_BY_EXPERT;
+    if (col) return Q4_0_ROUTE_BY_COLUMN;
+    return Q4_0_EUNSUPPORTED;
+}
+
+int q4_0_matmul_routed_ex(const void *experts, int64_t n_experts, const void *x, int x_dtype,
+                          const int32_t *route, int64_t k, float *y, int64_t n, int64_t out,
+                          int64_t in, int route_kernel, void *stream) {
     const int st = check_shape(n, out, in);
     if (st != Q4_0_OK) return st;
     if (x_dtype != Q4_0_F32 && x_dtype != Q4_0_F16) return Q4_0_EINVAL;
+    if (route_kernel != Q4_0_ROUTE_AUTO && route_kernel != Q4_0_ROUTE_BY_COLUMN &&
+        route_kernel != Q4_0_ROUTE_BY_EXPERT)
+        return Q4_0_EINVAL;
     if (n_experts < 1 || n_experts > Q4_0_MAX_EXPERTS || k < 1 || k > Q4_0_MAX_ROUTED)
         return Q4_0_EINVAL;
     if (!experts || !x || !route || !y) return Q4_0_ENULL;
@@ -261,15 +291,30 @@ int q4_0_matmul_routed(const void *experts, int64_t n_experts, const void *x, in
     if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, experts, wbytes) ||
         overlaps(y, ybytes, route, (size_t)pairs * 4u))
         return Q4_0_EALIAS;
-    if (!q4::gemv_mfma_routed_supports(pairs, out, in)) return Q4_0_EUNSUPPORTED;
+    int rk = route_kernel;
+    if (rk == Q4_0_ROUTE_AUTO) {
+        rk = q4_0_select_route(n, k, n_experts, out, in);
+        if (rk < 0) return rk;
+    } else if (rk == Q4_0_ROUTE_BY_COLUMN ? !q4::gemv_mfma_routed_supports(pairs, out, in)
+                                          : !q4::gemv_mfma_by_expert_supports(pairs, n_experts,
+                                                                              out, in)) {
+        return Q4_0_EUNSUPPORTED;
+    }
     const hipStream_t s = (hipStream_t)stream;
+    const size_t wsb = rk == Q4_0_ROUTE_BY_COLUMN
+                           ? q4::gemv_mfma_routed_workspace_bytes(pairs, out, in)
+                           : q4::gemv_mfma_by_expert_workspace_bytes(pairs, n_experts, out, in);
     void *ws = nullptr;
-    if (q4::gemv_mfma_routed_workspace_bytes(pairs, out, in) > 0) {
+    if (wsb > 0) {
         const int wst = get_workspace(s, &ws);
         if (wst != Q4_0_OK) return wst;
     }
-    return map_hip(q4::launch_gemv_mfma_routed(experts, n_experts, x, x_dtype == Q4_0_F16,
-                                               route, k, y, n, out, in, ws, s));
+    const int f16 = x_dtype == Q4_0_F16;
+    return map_hip(rk == Q4_0_ROUTE_BY_COLUMN
+                       ? q4::launch_gemv_mfma_routed(experts, n_experts, x, f16, route, k, y, n,
+                                                     out, in, ws, s)
+                       : q4::launch_gemv_mfma_by_expert(experts, n_experts, x, f16, route, k, y,
+                                                        n, out, in, ws, s));
 }
 
 int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int64_t n,

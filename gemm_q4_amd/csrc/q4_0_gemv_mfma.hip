@@ -176,14 +176,23 @@ struct GemvLinear {
 // A routed launch (mixture of experts, by column): lin[0] describes the
 // geometry of every expert; pair p = column * k + slot computes row p of y
 // from x row p / k and the expert route[p] of a stack of experts.
+//
+// By expert instead (chunk_expert set): the pairs routed to one expert are
+// gathered into chunks of kChunkRows rows (route_plan_kernel), each chunk is
+// one kChunkRows-row product with its expert, and wpp workgroups serve each
+// chunk; its row i lands in y row slot_pair[chunk * kChunkRows + i].
+constexpr int kChunkRows = 8;
 struct GemvRoute {
     const int32_t *route; // device, one expert index per pair; null: not routed
+    const int32_t *chunk_expert; // by expert: expert of each chunk (E: invalid, -1: unused)
+    const int32_t *slot_pair;    // by expert: pair of each chunk row (-1: padding)
     int64_t expert_bytes; // bytes from one expert's packed matrix to the next
     int64_t x_row_bytes;  // bytes from one x row to the next
-    int64_t part_pair;    // floats of partial sums per pair (K split), else 0
+    int64_t part_pair;    // floats of partial sums per pair or chunk (K split), else 0
+    int64_t frag_chunk;   // by expert: bytes of one chunk's prepared fragments
     int n_experts;
     int k;                // pairs per x row
-    int wpp;              // workgroups per pair
+    int wpp;              // workgroups per pair or chunk
 };
 
 struct GemvArgs {
@@ -297,13 +306,33 @@ __device__ __forceinline__ void load_item(const XT *row, int in, int it, float v
         v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
     }
 }
+//
+// Gathered (by-expert routing, chunk_expert set): workgroup w converts row
+// w % kChunkRows of chunk w / kChunkRows, the x row of pair slot_pair[w]
+// (zeros for padding), into that chunk's own fragments, chunk_bytes apart;
+// the workgroups of unused chunks return at once.
+struct XGather {
+    const int32_t *chunk_expert;
+    const int32_t *slot_pair;
+    int k;
+    int64_t chunk_bytes;
+};
 template <int NT, typename XT>
 __global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restrict__ x, int in,
-                                                             int nbpad,
-                                                             uint8_t *__restrict__ frag) {
+                                                             int nbpad, uint8_t *__restrict__ frag,
+                                                             const XGather gather) {
     __shared__ float wmax[kPrepThreads / 64];
-    const int t = blockIdx.x;
+    int t = blockIdx.x;
     const XT *row = x + (int64_t)t * in;
+    if (gather.chunk_expert) {
+        const int c = t / kChunkRows;
+        if (gather.chunk_expert[c] < 0) return;               // the whole workgroup
+        const int pr = gather.slot_pair[t];
+        frag += (int64_t)c * gather.chunk_bytes;
+        t -= c * kChunkRows;
+        row = x + (int64_t)(pr < 0 ? 0 : pr / gather.k) * in;
+        if (pr < 0) in = 0;                                   // padding: a zero row
+    }
     const int items = nbpad * 4;
     float v[kPrepItems][8];
     float m = 0.0f;
@@ -375,7 +404,19 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // routed launch: this pair's expert, x row, y row and partial sums; an
     // expert index outside the stack reads expert 0 and stores NaN
     bool bad_route = false;
-    if (args.rt.route) {
+    const int32_t *yslots = nullptr;      // by expert: this chunk's y rows
+    if (args.rt.chunk_expert) {
+        const int c = (int)blockIdx.x / args.rt.wpp;
+        local = (int)blockIdx.x - c * args.rt.wpp;
+        int e = __builtin_amdgcn_readfirstlane(args.rt.chunk_expert[c]);
+        if (e < 0) return;                // unused chunk: the whole workgroup, before any barrier
+        bad_route = e >= args.rt.n_experts;
+        if (bad_route) e = 0;
+        a.packed += (int64_t)e * args.rt.expert_bytes;
+        a.frag += (int64_t)c * args.rt.frag_chunk;
+        if (a.part) a.part += (int64_t)c * args.rt.part_pair;
+        yslots = args.rt.slot_pair + (int64_t)c * kChunkRows;
+    } else if (args.rt.route) {
         const int pair = (int)blockIdx.x / args.rt.wpp;
         local = (int)blockIdx.x - pair * args.rt.wpp;
         int e = __builtin_amdgcn_readfirstlane(args.rt.route[pair]);
@@ -660,7 +701,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                 const int row = t * kTileRows + rr;
                 if (row < a.out && tt < args.nrows) {
                     if (bad_route) sum = __builtin_nanf("");
-                    if (a.y) a.y[(int64_t)tt * a.out + row] = sum;
+                    const int64_t yr = yslots ? yslots[tt] : tt;   // padding: -1
+                    if (a.y && yr >= 0) a.y[yr * a.out + row] = sum;
                     if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
                         for (int u = 0; u < NT; ++u)
@@ -709,6 +751,7 @@ struct ReduceArgs {
     // partial sums part_pair floats and its y row out floats further on
     int64_t pair_elems;
     int64_t part_pair;
+    const int32_t *slot_pair;   // by expert: y row of each chunk row (-1: padding)
     int64_t total;
     uint2 *amax;         // per-workgroup (max, index) pairs of a single linear, or null
 };
@@ -732,11 +775,13 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
             if (f >= args.lin[k].e0) li = k;
         ReduceLinear L = args.lin[li];
         int64_t e = f - L.e0;
-        if (args.pair_elems > 0) {                   // routed: pair of element f
+        int64_t chunk = 0;
+        if (args.pair_elems > 0) {                   // routed: pair (chunk) of element f
             const int64_t pair = e / args.pair_elems;
             e -= pair * args.pair_elems;
             L.part += pair * args.part_pair;
-            L.y += pair * L.out;
+            if (args.slot_pair) chunk = pair;
+            else L.y += pair * L.out;
         }
         const int rr = (int)(e & 15);
         const int tt = (int)((e >> 4) % NT);
@@ -756,7 +801,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_reduce_kernel(const ReduceArgs 
         }
         const int64_t row = t * kTileRows + rr;
         if (row < L.out && tt < args.nrows) {
-            if (L.y) L.y[(int64_t)tt * L.out + row] = s;
+            const int64_t yr = args.slot_pair ? args.slot_pair[chunk * kChunkRows + tt] : tt;
+            if (L.y && yr >= 0) L.y[yr * L.out + row] = s;
             if constexpr (NT <= kArgmaxRows) {
 #pragma unroll
                 for (int u = 0; u < NT; ++u)
@@ -1031,10 +1077,24 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
     bool prep = true;
     // the linears of a group agree on the pre-pass (gemv_mfma_group_uniform)
     for (int i = 0; i < count; ++i) prep = prep && use_prep(nrows, probs[i].out, probs[i].in);
+    // by column: one unprepared row per pair; by expert: prepared chunks of kChunkRows rows
+    const bool by_expert = route && route->chunk_expert;
+    if (route && (by_expert ? (!prep || nrows != kChunkRows || NT != kChunkRows) : prep))
+        return hipErrorInvalidValue;
     for (int i = 0; i < count; ++i) {
         const GemvProblem &pr = probs[i];
-        const MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
+        MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
         const Layout L(pr.out, pr.in);
+        if (by_expert) {
+            // about kMfmaTargetWgs workgroups over all chunks: each chunk's x
+            // fragments are loaded once per workgroup, so a chunk takes few
+            // workgroups with long runs of tiles
+            int64_t gx = kMfmaTargetWgs / npairs_routed;
+            if (gx < 1) gx = 1;
+            if (gx > L.tiles) gx = L.tiles;
+            p.tpw = (L.tiles + gx - 1) / gx;
+            p.gx = (L.tiles + p.tpw - 1) / p.tpw;
+        }
         GemvLinear &g = a.lin[i];
         g.packed = (const uint8_t *)pr.packed;
         g.x = pr.x;
@@ -1053,9 +1113,10 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             rl.e0 = ra.total;
             ra.total += L.tiles * NT * 16;
             const int64_t pb = (int64_t)mfma_part_bytes(p, pr.out, pr.in);
-            if (route) {                            // each pair its own partial sums
+            if (route) {                            // each pair (chunk) its own partial sums
                 ra.pair_elems = L.tiles * NT * 16;
                 ra.part_pair = pb / (int64_t)sizeof(float);
+                ra.slot_pair = by_expert ? route->slot_pair : nullptr;
                 ra.total = ra.pair_elems * npairs_routed;
                 wsoff += pb * npairs_routed;
             } else {
@@ -1093,12 +1154,21 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             if (a.lin[i].frag) continue;
             uint8_t *f = (uint8_t *)ws + wsoff;
             a.lin[i].frag = f;
-            wsoff += frag_bytes(nrows, probs[i].in);
+            const int64_t fb = frag_bytes(nrows, probs[i].in);
+            XGather gth = {};
+            int64_t units = 1;
+            if (by_expert) {                        // each chunk its own fragments
+                gth = {route->chunk_expert, route->slot_pair, route->k, fb};
+                a.rt.frag_chunk = fb;
+                units = npairs_routed;
+            }
+            wsoff += fb * units;
             const int nbpad = a.lin[i].g4 * 4;
             // one workgroup per row of x (rows of the instance past nrows are
             // never read: their products land in outputs that are not stored)
-            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)nrows), dim3(kPrepThreads),
-                               0, stream, (const XT *)probs[i].x, (int)probs[i].in, nbpad, f);
+            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)(nrows * units)),
+                               dim3(kPrepThreads), 0, stream, (const XT *)probs[i].x,
+                               (int)probs[i].in, nbpad, f, gth);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1226,6 +1296,120 @@ hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Routed by expert: the plan.  One workgroup buckets the pairs p = t*k + j by
+// expert (an index outside [0, E) goes to bucket E), cuts each bucket into
+// chunks of kChunkRows rows and writes chunk_expert[c] (the bucket of chunk
+// c, -1 past the used chunks) and slot_pair[c * kChunkRows + i] (the pair in
+// row i of chunk c, -1 for padding).  A pair's place inside its bucket comes
+// from an LDS atomic and may change from call to call; the y row of every
+// pair does not, since the rows of a chunk's product are independent.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxPairs = 4096;
+constexpr int kPlanMaxBuckets = 4097;    // experts + the invalid bucket
+__global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
+    const int32_t *__restrict__ route, int pairs, int n_experts, int max_chunks,
+    int32_t *__restrict__ chunk_expert, int32_t *__restrict__ slot_pair) {
+    __shared__ int cnt[kPlanMaxBuckets];   // pairs per bucket, then first chunk of the bucket
+    __shared__ int bkt[kPlanMaxPairs];
+    __shared__ int rnk[kPlanMaxPairs];
+    __shared__ int scan[kPlanThreads];
+    const int tid = threadIdx.x;
+    const int nb = n_experts + 1;
+    for (int i = tid; i < nb; i += kPlanThreads) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < pairs; p += kPlanThreads) {
+        int e = route[p];
+        if (e < 0 || e >= n_experts) e = n_experts;
+        bkt[p] = e;
+        rnk[p] = atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    // chunks per bucket; exclusive scan over contiguous runs of buckets
+    const int seg = (nb + kPlanThreads - 1) / kPlanThreads;
+    const int s0 = tid * seg < nb ? tid * seg : nb;
+    const int s1 = s0 + seg < nb ? s0 + seg : nb;
+    int mine = 0;
+    for (int i = s0; i < s1; ++i) mine += (cnt[i] + kChunkRows - 1) / kChunkRows;
+    scan[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int used = scan[kPlanThreads - 1];
+    int base = scan[tid] - mine;
+    for (int i = s0; i < s1; ++i) {
+        const int c = cnt[i], nc = (c + kChunkRows - 1) / kChunkRows;
+        for (int q = 0; q < nc; ++q) chunk_expert[base + q] = i;
+        for (int q = c; q < nc * kChunkRows; ++q) slot_pair[(int64_t)base * kChunkRows + q] = -1;
+        cnt[i] = base;
+        base += nc;
+    }
+    __syncthreads();
+    for (int p = tid; p < pairs; p += kPlanThreads)
+        slot_pair[(int64_t)cnt[bkt[p]] * kChunkRows + rnk[p]] = p;
+    for (int c = used + tid; c < max_chunks; c += kPlanThreads) {
+        chunk_expert[c] = -1;
+        for (int q = 0; q < kChunkRows; ++q) slot_pair[(int64_t)c * kChunkRows + q] = -1;
+    }
+}
+
+// Chunks a by-expert call may use: each bucket's last chunk may be partial.
+static int64_t max_chunks(int64_t pairs, int64_t n_experts) {
+    const int64_t buckets = n_experts + 1 < pairs ? n_experts + 1 : pairs;
+    return (pairs + kChunkRows - 1) / kChunkRows + buckets;
+}
+
+// Workspace of a by-expert call: the plan's tables, then per chunk its
+// partial sums (K split) and its prepared fragments.
+static int64_t by_expert_table_bytes(int64_t chunks) {
+    return round256(chunks * 4) + round256(chunks * kChunkRows * 4);
+}
+size_t gemv_mfma_by_expert_workspace_bytes(int64_t pairs, int64_t n_experts, int64_t out,
+                                           int64_t in) {
+    const int64_t c = max_chunks(pairs, n_experts);
+    const MfmaPlan p = mfma_plan(kChunkRows, out, in);
+    return (size_t)(by_expert_table_bytes(c) +
+                    c * ((int64_t)mfma_part_bytes(p, out, in) + frag_bytes(kChunkRows, in)));
+}
+
+bool gemv_mfma_by_expert_supports(int64_t pairs, int64_t n_experts, int64_t out, int64_t in) {
+    if (pairs < 1 || pairs > kPlanMaxPairs || n_experts < 1 || n_experts + 1 > kPlanMaxBuckets)
+        return false;
+    if (!launch_supported(kChunkRows, out, in) || !use_prep(kChunkRows, out, in)) return false;
+    const MfmaPlan p = mfma_plan(kChunkRows, out, in);
+    return p.gx * p.slices * max_chunks(pairs, n_experts) <= 0x7fffffff &&
+           gemv_mfma_by_expert_workspace_bytes(pairs, n_experts, out, in) <= kWorkspaceBytes;
+}
+
+hipError_t launch_gemv_mfma_by_expert(const void *experts, int64_t n_experts, const void *x,
+                                      int x_f16, const int32_t *route, int64_t k, float *y,
+                                      int64_t n, int64_t out, int64_t in, void *ws,
+                                      hipStream_t stream) {
+    const int64_t pairs = n * k, chunks = max_chunks(pairs, n_experts);
+    int32_t *chunk_expert = (int32_t *)ws;
+    int32_t *slot_pair = (int32_t *)((uint8_t *)ws + round256(chunks * 4));
+    hipLaunchKernelGGL(route_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, route,
+                       (int)pairs, (int)n_experts, (int)chunks, chunk_expert, slot_pair);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemvRoute rt = {};
+    rt.chunk_expert = chunk_expert;
+    rt.slot_pair = slot_pair;
+    rt.expert_bytes = Layout(out, in).total_bytes();
+    rt.x_row_bytes = in * (x_f16 ? 2 : 4);
+    rt.n_experts = (int)n_experts;
+    rt.k = (int)k;
+    void *rest = (uint8_t *)ws + by_expert_table_bytes(chunks);
+    const GemvProblem p = {experts, x, y, out, in};
+    return x_f16 ? launch_mfma_t<kChunkRows, _Float16>(&p, 1, rest, stream, nullptr, nullptr,
+                                                       kChunkRows, &rt, chunks)
+                 : launch_mfma_t<kChunkRows, float>(&p, 1, rest, stream, nullptr, nullptr,
+                                                    kChunkRows, &rt, chunks);
 }
 
 // Routed (mixture of experts, by column): every (x row, expert) pair is a

@@ -168,9 +168,8 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
  * a column reads the matrices it was routed to, and the by-column kernels
  * take a column offset so that one pass answers several columns):
  *     y[t*k + j][o] = sum_i W_e[o][i] * x[t][i],   e = route[t*k + j],
- * for every column t < n and slot j < k, all n*k pairs in one launch of the
- * small-n MFMA kernel (one row each, with the precision of q4_0_matmul at
- * n = 1).
+ * for every column t < n and slot j < k, on the small-n MFMA kernel, by
+ * column or by expert as q4_0_select_route picks (q4_0_matmul_routed_ex).
  *   experts : DEVICE, n_experts repacked [out x in] matrices back to back,
  *             q4_0_packed_bytes(out, in) bytes apart, 16-byte aligned;
  *   x       : DEVICE [n x in] (x_dtype); route : DEVICE int32 [n x k];
@@ -185,6 +184,31 @@ int q4_0_matmul_grouped(const q4_0_linear *linears, int count, int x_dtype, int6
 int q4_0_matmul_routed(const void *experts, int64_t n_experts, const void *x, int x_dtype,
                        const int32_t *route, int64_t k, float *y, int64_t n, int64_t out,
                        int64_t in, void *stream);
+
+/* The routed product with its form chosen by the caller (golem-server README,
+ * "On the card": by column, every pair reads its expert; by expert, a prompt
+ * reads each expert once for the columns routed to it):
+ *   Q4_0_ROUTE_BY_COLUMN : one one-row product per pair, all in one launch;
+ *   Q4_0_ROUTE_BY_EXPERT : a one-workgroup plan kernel buckets the pairs by
+ *       expert on the device and cuts each bucket into chunks of 8 rows; each
+ *       chunk is one 8-row product with its expert (x as binary16 high and
+ *       low parts, as q4_0_matmul at n = 8), its rows stored to their pairs'
+ *       y rows.  Needs n*k <= 4096;
+ *   Q4_0_ROUTE_AUTO      : by expert from a measured number of x rows up,
+ *       by column below (q4_0_select_route).
+ * Both forms give each pair's row to the small-n tolerance of the oracle; a
+ * pair's row does not depend on the other pairs.  Arguments and errors as
+ * q4_0_matmul_routed, plus Q4_0_EINVAL for an unknown route_kernel and
+ * Q4_0_EUNSUPPORTED when the chosen form cannot take the call. */
+#define Q4_0_ROUTE_AUTO 0
+#define Q4_0_ROUTE_BY_COLUMN 1
+#define Q4_0_ROUTE_BY_EXPERT 2
+int q4_0_matmul_routed_ex(const void *experts, int64_t n_experts, const void *x, int x_dtype,
+                          const int32_t *route, int64_t k, float *y, int64_t n, int64_t out,
+                          int64_t in, int route_kernel, void *stream);
+/* The form Q4_0_ROUTE_AUTO takes for these sizes (a Q4_0_ROUTE_* value), or
+ * a negative status (Q4_0_ESHAPE, Q4_0_EINVAL, Q4_0_EUNSUPPORTED). */
+int q4_0_select_route(int64_t n, int64_t k, int64_t n_experts, int64_t out, int64_t in);
 
 /* Logit-head product with its epilogue fused: y = x . W^T as in
  * q4_0_matmul (small-n kernel, n <= 8), and for every row t of y its largest

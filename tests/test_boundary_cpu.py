@@ -263,3 +263,19 @@ def test_routed_validation():
     assert status_of(f, A16, 4, B16, q4.F32, C16, 2, B16 + 16, 1, 10, 64, 0) == q4.EALIAS
     assert status_of(f, A16, 4, B16, q4.F32, C16, 2, A16 + 64, 1, 10, 64, 0) == q4.EALIAS
     assert status_of(f, A16, 4, B16, q4.F32, E16, 2, E16 - 64, 1, 10, 64, 0) == q4.EALIAS
+
+
+def test_routed_ex_and_route_choice():
+    D16 = 1 << 38
+    f = q4.q4_0_matmul_routed_ex
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, D16, 1, 10, 64, 3, 0) == q4.EINVAL
+    # by expert takes at most 4096 pairs
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 64, D16, 65, 10, 64, q4.ROUTE_BY_EXPERT,
+                     0) == q4.EUNSUPPORTED
+    sel = q4._lib.q4_0_select_route
+    assert sel(1, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
+    assert sel(16, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
+    assert sel(32, 8, 128, 768, 2048) == q4.ROUTE_BY_EXPERT
+    assert sel(65, 64, 128, 768, 2048) == q4.ROUTE_BY_COLUMN    # too many pairs by expert
+    assert sel(1, 0, 128, 768, 2048) == q4.EINVAL
+    assert sel(1, 8, 128, 768, 48) == q4.ESHAPE

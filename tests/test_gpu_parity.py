@@ -681,3 +681,64 @@ def test_routed_moe_full_size_sampled_rows():
         for j in range(k):
             p, e = t * k + j, int(route[t, j])
             assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_, rows=rows) <= TOL_SMALL_N
+
+
+# ------------------------------------------------------------------ routed (by expert)
+@pytest.mark.parametrize("n,k,out,in_", [(3, 2, 300, 160), (20, 4, 37, 4128),
+                                         (9, 3, 64, 9728)])
+@pytest.mark.parametrize("xdt", [np.float32, np.float16], ids=["xf32", "xf16"])
+def test_routed_by_expert_equals_8_row_calls_and_oracle(n, k, out, in_, xdt):
+    """By expert, each pair's row equals row 0 of the 8-row product of its
+    expert with its x row (the chunk's instance) bit for bit, whichever chunk
+    and row the plan gave it, and matches the oracle.  Six experts for up to
+    80 pairs: buckets of several chunks, partial last chunks."""
+    n_exp = 6
+    blks, stack = _expert_stack(n_exp, out, in_, seed=100)
+    x = synth.make_x(n, in_, seed=101, dtype=xdt)
+    route = np.random.default_rng(102).integers(0, n_exp, size=(n, k)).astype(np.int32)
+    yd = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out,
+                          route_kernel=q4.ROUTE_BY_EXPERT)
+    y2 = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out,
+                          route_kernel=q4.ROUTE_BY_EXPERT)
+    torch.cuda.synchronize()
+    yy = yd.cpu().numpy()
+    assert np.array_equal(yy, y2.cpu().numpy())          # the plan's order does not matter
+    pb = q4.q4_0_packed_bytes(out, in_)
+    for t in range(n):
+        x8 = np.repeat(x[t:t + 1], 8, axis=0)
+        for j in range(k):
+            p, e = t * k + j, int(route[t, j])
+            single = run(stack[e * pb:(e + 1) * pb], x8, out, kernel=q4.KERNEL_GEMV_MFMA)
+            assert np.array_equal(yy[p], single[0]), (t, j, e)
+            assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_) <= TOL_SMALL_N
+
+
+def test_routed_by_expert_index_outside_the_stack_gives_nan_rows():
+    out, in_, n_exp = 100, 4128, 3
+    blks, stack = _expert_stack(n_exp, out, in_, seed=110)
+    x = synth.make_x(3, in_, seed=111)
+    route = np.array([[0, -1], [n_exp, 2], [2, 7]], dtype=np.int32)
+    yy = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out,
+                          route_kernel=q4.ROUTE_BY_EXPERT).cpu().numpy()
+    assert np.isnan(yy[[1, 2, 5]]).all()
+    for p, t, e in [(0, 0, 0), (3, 1, 2), (4, 2, 2)]:
+        assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("n", [32, 64])
+def test_routed_moe_by_expert_full_size_sampled_rows(n):
+    """The synthetic mixture-of-experts up projection (128 experts of 768 x
+    2048, 8 distinct experts per row) by expert, as AUTO takes it at these
+    row counts; sampled output rows against the oracle."""
+    out, in_, n_exp, k = 768, 2048, 128, 8
+    assert q4.q4_0_select_route(n, k, n_exp, out, in_) == q4.ROUTE_BY_EXPERT
+    blks, stack = _expert_stack(n_exp, out, in_, seed=90)
+    x = synth.make_x(n, in_, seed=121)
+    rng = np.random.default_rng(122)
+    route = np.stack([rng.permutation(n_exp)[:k] for _ in range(n)]).astype(np.int32)
+    yy = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out).cpu().numpy()
+    rows = np.arange(5, out, 13)
+    for t in range(0, n, 3):
+        for j in range(k):
+            p, e = t * k + j, int(route[t, j])
+            assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_, rows=rows) <= TOL_SMALL_N
