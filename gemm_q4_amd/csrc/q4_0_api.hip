@@ -75,8 +75,8 @@ constexpr int64_t kSmallNMax = 64;
 // that chose it, the two crossing near thirty-two columns): by expert from
 // this many x rows, by column below.  Measured on MI355X (128 experts of 768 x
 // 2048, 8 per row, graph replay), by column against by expert: n = 1 4.7 /
-// 12.9 us, n = 8 15.4 / 30.9, n = 16 28.6 / 39.9, n = 32 49.5 / 47.6, n = 64
-// 89.9 / 54.2.
+// 12.9 us, n = 8 15.0 / 28.1, n = 16 27.5 / 38.3, n = 32 48.2 / 41.7, n = 64
+// 87.6 / 46.1.
 constexpr int64_t kByExpertMinN = 32;
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (n <= kSmallNMax && q4::gemv_mfma_supports(n, out, in, x_f16))
