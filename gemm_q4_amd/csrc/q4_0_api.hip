@@ -75,9 +75,9 @@ constexpr int64_t kSmallNMax = 64;
 // that chose it, the two crossing near thirty-two columns): by expert from
 // this many x rows, by column below.  Measured on MI355X (128 experts of 768 x
 // 2048, 8 per row, graph replay), by column against by expert: n = 1 4.7 /
-// 12.9 us, n = 8 15.0 / 28.1, n = 16 27.5 / 38.3, n = 32 48.2 / 41.7, n = 64
-// 87.6 / 46.1.
-constexpr int64_t kByExpertMinN = 32;
+// 12.9 us, n = 8 14.9 / 19.3, n = 16 27.7 / 26.7, n = 24 38.4 / 28.9, n = 32
+// 48.5 / 29.0, n = 64 87.9 / 36.2: the crossover sits at 16 rows on this part.
+constexpr int64_t kByExpertMinN = 16;
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (n <= kSmallNMax && q4::gemv_mfma_supports(n, out, in, x_f16))
         return Q4_0_KERNEL_GEMV_MFMA;
@@ -264,7 +264,7 @@ int q4_0_select_route(int64_t n, int64_t k, int64_t n_experts, int64_t out, int6
     if (n_experts < 1 || n_experts > Q4_0_MAX_EXPERTS || k < 1 || k > Q4_0_MAX_ROUTED)
         return Q4_0_EINVAL;
     const bool col = q4::gemv_mfma_routed_supports(n * k, out, in);
-    const bool exp = q4::gemv_mfma_by_expert_supports(n * k, n_experts, out, in);
+    const bool exp = q4::gemv_mfma_by_expert_supports(n, k, n_experts, out, in);
     if (exp && (n >= kByExpertMinN || !col)) return Q4_0_ROUTE_BY_EXPERT;
     if (col) return Q4_0_ROUTE_BY_COLUMN;
     return Q4_0_EUNSUPPORTED;
@@ -296,14 +296,14 @@ int q4_0_matmul_routed_ex(const void *experts, int64_t n_experts, const void *x,
         rk = q4_0_select_route(n, k, n_experts, out, in);
         if (rk < 0) return rk;
     } else if (rk == Q4_0_ROUTE_BY_COLUMN ? !q4::gemv_mfma_routed_supports(pairs, out, in)
-                                          : !q4::gemv_mfma_by_expert_supports(pairs, n_experts,
+                                          : !q4::gemv_mfma_by_expert_supports(n, k, n_experts,
                                                                               out, in)) {
         return Q4_0_EUNSUPPORTED;
     }
     const hipStream_t s = (hipStream_t)stream;
     const size_t wsb = rk == Q4_0_ROUTE_BY_COLUMN
                            ? q4::gemv_mfma_routed_workspace_bytes(pairs, out, in)
-                           : q4::gemv_mfma_by_expert_workspace_bytes(pairs, n_experts, out, in);
+                           : q4::gemv_mfma_by_expert_workspace_bytes(n, k, n_experts, out, in);
     void *ws = nullptr;
     if (wsb > 0) {
         const int wst = get_workspace(s, &ws);

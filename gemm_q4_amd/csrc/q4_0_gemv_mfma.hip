@@ -178,9 +178,10 @@ struct GemvLinear {
 // from x row p / k and the expert route[p] of a stack of experts.
 //
 // By expert instead (chunk_expert set): the pairs routed to one expert are
-// gathered into chunks of kChunkRows rows (route_plan_kernel), each chunk is
+// bucketed into chunks of kChunkRows rows (route_plan), each chunk is
 // one kChunkRows-row product with its expert, and wpp workgroups serve each
-// chunk; its row i lands in y row slot_pair[chunk * kChunkRows + i].
+// chunk; row i of a chunk reads the prepared fragments of x row
+// slot_pair[chunk * kChunkRows + i] / k and lands in y row slot_pair[...].
 constexpr int kChunkRows = 8;
 struct GemvRoute {
     const int32_t *route; // device, one expert index per pair; null: not routed
@@ -189,10 +190,11 @@ struct GemvRoute {
     int64_t expert_bytes; // bytes from one expert's packed matrix to the next
     int64_t x_row_bytes;  // bytes from one x row to the next
     int64_t part_pair;    // floats of partial sums per pair or chunk (K split), else 0
-    int64_t frag_chunk;   // by expert: bytes of one chunk's prepared fragments
+    int64_t frag_chunk;   // by expert: bytes of one 8-row region of prepared x fragments
     int n_experts;
     int k;                // pairs per x row
     int wpp;              // workgroups per pair or chunk
+    int x_rows;           // by expert: rows of x (host side, sizes the pre-pass)
 };
 
 struct GemvArgs {
@@ -307,31 +309,26 @@ __device__ __forceinline__ void load_item(const XT *row, int in, int it, float v
     }
 }
 //
-// Gathered (by-expert routing, chunk_expert set): workgroup w converts row
-// w % kChunkRows of chunk w / kChunkRows, the x row of pair slot_pair[w]
-// (zeros for padding), into that chunk's own fragments, chunk_bytes apart;
-// the workgroups of unused chunks return at once.
-struct XGather {
-    const int32_t *chunk_expert;
-    const int32_t *slot_pair;
-    int k;
-    int64_t chunk_bytes;
+// In regions (region_bytes set, by-expert routing): workgroup w converts x
+// row w (zeros past x_rows) as row w % 8 of its own 8-row region of
+// fragments, region w / 8, region_bytes apart.
+struct XRegions {
+    int64_t region_bytes;
+    int x_rows;
 };
 template <int NT, typename XT>
-__global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restrict__ x, int in,
-                                                             int nbpad, uint8_t *__restrict__ frag,
-                                                             const XGather gather) {
+__device__ __forceinline__ void xprep_row(const XT *__restrict__ x, int in, int nbpad,
+                                          uint8_t *__restrict__ frag, const XRegions reg,
+                                          int t) {
     __shared__ float wmax[kPrepThreads / 64];
-    int t = blockIdx.x;
     const XT *row = x + (int64_t)t * in;
-    if (gather.chunk_expert) {
-        const int c = t / kChunkRows;
-        if (gather.chunk_expert[c] < 0) return;               // the whole workgroup
-        const int pr = gather.slot_pair[t];
-        frag += (int64_t)c * gather.chunk_bytes;
-        t -= c * kChunkRows;
-        row = x + (int64_t)(pr < 0 ? 0 : pr / gather.k) * in;
-        if (pr < 0) in = 0;                                   // padding: a zero row
+    if (reg.region_bytes) {
+        if (t >= reg.x_rows) {                                // padding: a zero row
+            row = x;
+            in = 0;
+        }
+        frag += (int64_t)(t / kChunkRows) * reg.region_bytes;
+        t %= kChunkRows;
     }
     const int items = nbpad * 4;
     float v[kPrepItems][8];
@@ -380,6 +377,88 @@ __global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restric
     }
 }
 
+template <int NT, typename XT>
+__global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restrict__ x, int in,
+                                                             int nbpad, uint8_t *__restrict__ frag,
+                                                             const XRegions reg) {
+    xprep_row<NT, XT>(x, in, nbpad, frag, reg, (int)blockIdx.x);
+}
+
+// Routed by expert: the plan.  One workgroup (of kPlanThreads) buckets the pairs p = t*k + j by
+// expert (an index outside [0, E) goes to bucket E), cuts each bucket into
+// chunks of kChunkRows rows and writes chunk_expert[c] (the bucket of chunk
+// c, -1 past the used chunks) and slot_pair[c * kChunkRows + i] (the pair in
+// row i of chunk c, -1 for padding).  A pair's place inside its bucket comes
+// from an LDS atomic and may change from call to call; the y row of every
+// pair does not, since the rows of a chunk's product are independent.
+constexpr int kPlanThreads = kPrepThreads;   // the plan runs as workgroup 0 of the pre-pass
+constexpr int kPlanMaxPairs = 4096;
+constexpr int kPlanMaxBuckets = 4097;    // experts + the invalid bucket
+__device__ __forceinline__ void route_plan(const int32_t *__restrict__ route, int pairs,
+                                           int n_experts, int max_chunks,
+                                           int32_t *__restrict__ chunk_expert,
+                                           int32_t *__restrict__ slot_pair) {
+    __shared__ int cnt[kPlanMaxBuckets];   // pairs per bucket, then first chunk of the bucket
+    __shared__ int bkt[kPlanMaxPairs];
+    __shared__ int rnk[kPlanMaxPairs];
+    __shared__ int scan[kPlanThreads];
+    const int tid = threadIdx.x;
+    const int nb = n_experts + 1;
+    for (int i = tid; i < nb; i += kPlanThreads) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < pairs; p += kPlanThreads) {
+        int e = route[p];
+        if (e < 0 || e >= n_experts) e = n_experts;
+        bkt[p] = e;
+        rnk[p] = atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    // chunks per bucket; exclusive scan over contiguous runs of buckets
+    const int seg = (nb + kPlanThreads - 1) / kPlanThreads;
+    const int s0 = tid * seg < nb ? tid * seg : nb;
+    const int s1 = s0 + seg < nb ? s0 + seg : nb;
+    int mine = 0;
+    for (int i = s0; i < s1; ++i) mine += (cnt[i] + kChunkRows - 1) / kChunkRows;
+    scan[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int used = scan[kPlanThreads - 1];
+    int base = scan[tid] - mine;
+    for (int i = s0; i < s1; ++i) {
+        const int c = cnt[i], nc = (c + kChunkRows - 1) / kChunkRows;
+        for (int q = 0; q < nc; ++q) chunk_expert[base + q] = i;
+        for (int q = c; q < nc * kChunkRows; ++q) slot_pair[(int64_t)base * kChunkRows + q] = -1;
+        cnt[i] = base;
+        base += nc;
+    }
+    __syncthreads();
+    for (int p = tid; p < pairs; p += kPlanThreads)
+        slot_pair[(int64_t)cnt[bkt[p]] * kChunkRows + rnk[p]] = p;
+    for (int c = used + tid; c < max_chunks; c += kPlanThreads) {
+        chunk_expert[c] = -1;
+        for (int q = 0; q < kChunkRows; ++q) slot_pair[(int64_t)c * kChunkRows + q] = -1;
+    }
+}
+
+// The by-expert pre-pass: workgroup 0 makes the plan, workgroup 1 + w
+// converts x row w into its region (the two do not depend on each other).
+template <int NT, typename XT>
+__global__ __launch_bounds__(kPrepThreads) void route_prep_kernel(
+    const int32_t *__restrict__ route, int pairs, int n_experts, int max_chunks,
+    int32_t *__restrict__ chunk_expert, int32_t *__restrict__ slot_pair,
+    const XT *__restrict__ x, int in, int nbpad, uint8_t *__restrict__ frag,
+    const XRegions reg) {
+    if (blockIdx.x == 0)
+        route_plan(route, pairs, n_experts, max_chunks, chunk_expert, slot_pair);
+    else
+        xprep_row<NT, XT>(x, in, nbpad, frag, reg, (int)blockIdx.x - 1);
+}
+
 // A-fragment store of one wave (unprepared launches): for block bl of the
 // wave's range, slot j and quarter g as in xprep_kernel, 16 bytes at
 // ((bl * 2*NT + j) * 4 + g) * 16 of the wave's LDS region.  A prepared launch
@@ -413,7 +492,6 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
         bad_route = e >= args.rt.n_experts;
         if (bad_route) e = 0;
         a.packed += (int64_t)e * args.rt.expert_bytes;
-        a.frag += (int64_t)c * args.rt.frag_chunk;
         if (a.part) a.part += (int64_t)c * args.rt.part_pair;
         yslots = args.rt.slot_pair + (int64_t)c * kChunkRows;
     } else if (args.rt.route) {
@@ -472,6 +550,14 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     h8_t afr_x[kXG][kRG > 1 ? GPW : 1][4];
     if constexpr (PREP) {
         const uint8_t *fb = a.frag + kFragHeader + (jslot * 4 + g) * 16;
+        if (yslots) {
+            // by expert (8 rows, split): slot j holds the high (j < 8) or low
+            // part of chunk row j % 8, whose x row has its own region
+            const int pr = yslots[jslot & 7];
+            const int xr = pr < 0 ? 0 : pr / args.rt.k;       // padding: row 0, never stored
+            fb = a.frag + (int64_t)(xr / kChunkRows) * args.rt.frag_chunk + kFragHeader +
+                 (((jslot & 8) + xr % kChunkRows) * 4 + g) * 16;
+        }
 #pragma unroll
         for (int q = 0; q < GPW; ++q)
 #pragma unroll
@@ -595,6 +681,12 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
         for (int j = 0; j < kXG; ++j) inv_x[j][i] = 1.0f;
         if constexpr (PREP) {
             inv[i] = row < NT ? reinterpret_cast<const float *>(a.frag)[row] : 1.0f;
+            if (yslots && row < NT) {
+                const int pr = yslots[row];
+                const int xr = pr < 0 ? 0 : pr / args.rt.k;
+                inv[i] = reinterpret_cast<const float *>(
+                    a.frag + (int64_t)(xr / kChunkRows) * args.rt.frag_chunk)[xr % kChunkRows];
+            }
             if constexpr (kRG > 1) {
 #pragma unroll
                 for (int j = 0; j < kRG - 1; ++j) {
@@ -1155,20 +1247,28 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             uint8_t *f = (uint8_t *)ws + wsoff;
             a.lin[i].frag = f;
             const int64_t fb = frag_bytes(nrows, probs[i].in);
-            XGather gth = {};
+            XRegions reg = {};
             int64_t units = 1;
-            if (by_expert) {                        // each chunk its own fragments
-                gth = {route->chunk_expert, route->slot_pair, route->k, fb};
+            if (by_expert) {                        // every x row once, 8-row regions
+                units = (route->x_rows + kChunkRows - 1) / kChunkRows;
+                reg = {fb, route->x_rows};
                 a.rt.frag_chunk = fb;
-                units = npairs_routed;
             }
             wsoff += fb * units;
             const int nbpad = a.lin[i].g4 * 4;
             // one workgroup per row of x (rows of the instance past nrows are
             // never read: their products land in outputs that are not stored)
-            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)(nrows * units)),
-                               dim3(kPrepThreads), 0, stream, (const XT *)probs[i].x,
-                               (int)probs[i].in, nbpad, f, gth);
+            if (by_expert)
+                hipLaunchKernelGGL((route_prep_kernel<NT, XT>),
+                                   dim3((unsigned)(1 + nrows * units)), dim3(kPrepThreads), 0,
+                                   stream, route->route, route->x_rows * route->k,
+                                   route->n_experts, (int)npairs_routed,
+                                   (int32_t *)route->chunk_expert, (int32_t *)route->slot_pair,
+                                   (const XT *)probs[i].x, (int)probs[i].in, nbpad, f, reg);
+            else
+                hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)(nrows * units)),
+                                   dim3(kPrepThreads), 0, stream, (const XT *)probs[i].x,
+                                   (int)probs[i].in, nbpad, f, reg);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1298,92 +1398,34 @@ hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float 
     return hipSuccess;
 }
 
-// Routed by expert: the plan.  One workgroup buckets the pairs p = t*k + j by
-// expert (an index outside [0, E) goes to bucket E), cuts each bucket into
-// chunks of kChunkRows rows and writes chunk_expert[c] (the bucket of chunk
-// c, -1 past the used chunks) and slot_pair[c * kChunkRows + i] (the pair in
-// row i of chunk c, -1 for padding).  A pair's place inside its bucket comes
-// from an LDS atomic and may change from call to call; the y row of every
-// pair does not, since the rows of a chunk's product are independent.
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanMaxPairs = 4096;
-constexpr int kPlanMaxBuckets = 4097;    // experts + the invalid bucket
-__global__ __launch_bounds__(kPlanThreads) void route_plan_kernel(
-    const int32_t *__restrict__ route, int pairs, int n_experts, int max_chunks,
-    int32_t *__restrict__ chunk_expert, int32_t *__restrict__ slot_pair) {
-    __shared__ int cnt[kPlanMaxBuckets];   // pairs per bucket, then first chunk of the bucket
-    __shared__ int bkt[kPlanMaxPairs];
-    __shared__ int rnk[kPlanMaxPairs];
-    __shared__ int scan[kPlanThreads];
-    const int tid = threadIdx.x;
-    const int nb = n_experts + 1;
-    for (int i = tid; i < nb; i += kPlanThreads) cnt[i] = 0;
-    __syncthreads();
-    for (int p = tid; p < pairs; p += kPlanThreads) {
-        int e = route[p];
-        if (e < 0 || e >= n_experts) e = n_experts;
-        bkt[p] = e;
-        rnk[p] = atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-    // chunks per bucket; exclusive scan over contiguous runs of buckets
-    const int seg = (nb + kPlanThreads - 1) / kPlanThreads;
-    const int s0 = tid * seg < nb ? tid * seg : nb;
-    const int s1 = s0 + seg < nb ? s0 + seg : nb;
-    int mine = 0;
-    for (int i = s0; i < s1; ++i) mine += (cnt[i] + kChunkRows - 1) / kChunkRows;
-    scan[tid] = mine;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    const int used = scan[kPlanThreads - 1];
-    int base = scan[tid] - mine;
-    for (int i = s0; i < s1; ++i) {
-        const int c = cnt[i], nc = (c + kChunkRows - 1) / kChunkRows;
-        for (int q = 0; q < nc; ++q) chunk_expert[base + q] = i;
-        for (int q = c; q < nc * kChunkRows; ++q) slot_pair[(int64_t)base * kChunkRows + q] = -1;
-        cnt[i] = base;
-        base += nc;
-    }
-    __syncthreads();
-    for (int p = tid; p < pairs; p += kPlanThreads)
-        slot_pair[(int64_t)cnt[bkt[p]] * kChunkRows + rnk[p]] = p;
-    for (int c = used + tid; c < max_chunks; c += kPlanThreads) {
-        chunk_expert[c] = -1;
-        for (int q = 0; q < kChunkRows; ++q) slot_pair[(int64_t)c * kChunkRows + q] = -1;
-    }
-}
-
 // Chunks a by-expert call may use: each bucket's last chunk may be partial.
 static int64_t max_chunks(int64_t pairs, int64_t n_experts) {
     const int64_t buckets = n_experts + 1 < pairs ? n_experts + 1 : pairs;
     return (pairs + kChunkRows - 1) / kChunkRows + buckets;
 }
 
-// Workspace of a by-expert call: the plan's tables, then per chunk its
-// partial sums (K split) and its prepared fragments.
+// Workspace of a by-expert call: the plan's tables, per chunk its partial
+// sums (K split), then the prepared fragments of x in 8-row regions.
 static int64_t by_expert_table_bytes(int64_t chunks) {
     return round256(chunks * 4) + round256(chunks * kChunkRows * 4);
 }
-size_t gemv_mfma_by_expert_workspace_bytes(int64_t pairs, int64_t n_experts, int64_t out,
+size_t gemv_mfma_by_expert_workspace_bytes(int64_t n, int64_t k, int64_t n_experts, int64_t out,
                                            int64_t in) {
-    const int64_t c = max_chunks(pairs, n_experts);
+    const int64_t c = max_chunks(n * k, n_experts);
     const MfmaPlan p = mfma_plan(kChunkRows, out, in);
-    return (size_t)(by_expert_table_bytes(c) +
-                    c * ((int64_t)mfma_part_bytes(p, out, in) + frag_bytes(kChunkRows, in)));
+    return (size_t)(by_expert_table_bytes(c) + c * (int64_t)mfma_part_bytes(p, out, in) +
+                    (n + kChunkRows - 1) / kChunkRows * frag_bytes(kChunkRows, in));
 }
 
-bool gemv_mfma_by_expert_supports(int64_t pairs, int64_t n_experts, int64_t out, int64_t in) {
+bool gemv_mfma_by_expert_supports(int64_t n, int64_t k, int64_t n_experts, int64_t out,
+                                  int64_t in) {
+    const int64_t pairs = n * k;
     if (pairs < 1 || pairs > kPlanMaxPairs || n_experts < 1 || n_experts + 1 > kPlanMaxBuckets)
         return false;
     if (!launch_supported(kChunkRows, out, in) || !use_prep(kChunkRows, out, in)) return false;
     const MfmaPlan p = mfma_plan(kChunkRows, out, in);
     return p.gx * p.slices * max_chunks(pairs, n_experts) <= 0x7fffffff &&
-           gemv_mfma_by_expert_workspace_bytes(pairs, n_experts, out, in) <= kWorkspaceBytes;
+           gemv_mfma_by_expert_workspace_bytes(n, k, n_experts, out, in) <= kWorkspaceBytes;
 }
 
 hipError_t launch_gemv_mfma_by_expert(const void *experts, int64_t n_experts, const void *x,
@@ -1393,17 +1435,15 @@ hipError_t launch_gemv_mfma_by_expert(const void *experts, int64_t n_experts, co
     const int64_t pairs = n * k, chunks = max_chunks(pairs, n_experts);
     int32_t *chunk_expert = (int32_t *)ws;
     int32_t *slot_pair = (int32_t *)((uint8_t *)ws + round256(chunks * 4));
-    hipLaunchKernelGGL(route_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, route,
-                       (int)pairs, (int)n_experts, (int)chunks, chunk_expert, slot_pair);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     GemvRoute rt = {};
+    rt.route = route;                     // read by the plan, in the pre-pass launch
     rt.chunk_expert = chunk_expert;
     rt.slot_pair = slot_pair;
     rt.expert_bytes = Layout(out, in).total_bytes();
     rt.x_row_bytes = in * (x_f16 ? 2 : 4);
     rt.n_experts = (int)n_experts;
     rt.k = (int)k;
+    rt.x_rows = (int)n;
     void *rest = (uint8_t *)ws + by_expert_table_bytes(chunks);
     const GemvProblem p = {experts, x, y, out, in};
     return x_f16 ? launch_mfma_t<kChunkRows, _Float16>(&p, 1, rest, stream, nullptr, nullptr,

@@ -65,11 +65,12 @@ hipError_t launch_gemv_mfma_routed(const void *experts, int64_t n_experts, const
                                    int x_f16, const int32_t *route, int64_t k, float *y,
                                    int64_t n, int64_t out, int64_t in, void *ws,
                                    hipStream_t stream);
-// By expert: the pairs routed to each expert are gathered on the device into
+// By expert: the pairs routed to each expert are bucketed on the device into
 // chunks of 8 rows, each chunk one prepared 8-row product with its expert.
-size_t gemv_mfma_by_expert_workspace_bytes(int64_t pairs, int64_t n_experts, int64_t out,
+size_t gemv_mfma_by_expert_workspace_bytes(int64_t n, int64_t k, int64_t n_experts, int64_t out,
                                            int64_t in);
-bool gemv_mfma_by_expert_supports(int64_t pairs, int64_t n_experts, int64_t out, int64_t in);
+bool gemv_mfma_by_expert_supports(int64_t n, int64_t k, int64_t n_experts, int64_t out,
+                                  int64_t in);
 hipError_t launch_gemv_mfma_by_expert(const void *experts, int64_t n_experts, const void *x,
                                       int x_f16, const int32_t *route, int64_t k, float *y,
                                       int64_t n, int64_t out, int64_t in, void *ws,

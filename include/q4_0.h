@@ -189,11 +189,12 @@ int q4_0_matmul_routed(const void *experts, int64_t n_experts, const void *x, in
  * "On the card": by column, every pair reads its expert; by expert, a prompt
  * reads each expert once for the columns routed to it):
  *   Q4_0_ROUTE_BY_COLUMN : one one-row product per pair, all in one launch;
- *   Q4_0_ROUTE_BY_EXPERT : a one-workgroup plan kernel buckets the pairs by
- *       expert on the device and cuts each bucket into chunks of 8 rows; each
- *       chunk is one 8-row product with its expert (x as binary16 high and
- *       low parts, as q4_0_matmul at n = 8), its rows stored to their pairs'
- *       y rows.  Needs n*k <= 4096;
+ *   Q4_0_ROUTE_BY_EXPERT : one workgroup of a pre-pass buckets the pairs
+ *       by expert on the device and cuts each bucket into chunks of 8 rows
+ *       while the others convert each x row once (binary16 high and low
+ *       parts, as q4_0_matmul at n = 8); then each chunk is one 8-row
+ *       product with its expert, its rows stored to their pairs' y rows.
+ *       Needs n*k <= 4096;
  *   Q4_0_ROUTE_AUTO      : by expert from a measured number of x rows up,
  *       by column below (q4_0_select_route).
  * Both forms give each pair's row to the small-n tolerance of the oracle; a
