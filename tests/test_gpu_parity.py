@@ -742,3 +742,34 @@ def test_routed_moe_by_expert_full_size_sampled_rows(n):
         for j in range(k):
             p, e = t * k + j, int(route[t, j])
             assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_, rows=rows) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("rk", [q4.ROUTE_BY_COLUMN, q4.ROUTE_BY_EXPERT], ids=["column", "expert"])
+def test_routed_graph_replay_follows_the_routing_table(rk):
+    """The routing stays on the device: one captured call, replayed after the
+    routing table is rewritten in place, gives each new routing's eager
+    result (K split, so the reduction kernel is in the graph too)."""
+    out, in_, n_exp, n, k = 100, 4128, 5, 18, 3
+    _, stack = _expert_stack(n_exp, out, in_, seed=130)
+    x = to_dev(synth.make_x(n, in_, seed=131))
+    rng = np.random.default_rng(132)
+    routes = [rng.integers(0, n_exp, size=(n, k)).astype(np.int32) for _ in range(3)]
+    route = to_dev(routes[0])
+    y = torch.zeros((n * k, out), dtype=torch.float32, device=DEV)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        q4.matmul_routed(stack, n_exp, x, route, out, y=y, route_kernel=rk)
+    cs.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        q4.matmul_routed(stack, n_exp, x, route, out, y=y, route_kernel=rk)
+    for rep in range(6):
+        r = routes[rep % 3]
+        route.copy_(to_dev(r))
+        ref = q4.matmul_routed(stack, n_exp, x, to_dev(r), out, route_kernel=rk)
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), rep
