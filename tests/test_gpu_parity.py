@@ -773,3 +773,25 @@ def test_routed_graph_replay_follows_the_routing_table(rk):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, ref), rep
+
+
+@pytest.mark.parametrize("rk", [q4.ROUTE_BY_COLUMN, q4.ROUTE_BY_EXPERT], ids=["column", "expert"])
+@pytest.mark.parametrize("n_exp,n,k,out,in_,xdt", [
+    (1, 5, 3, 37, 96, np.float32),                       # one expert takes every pair
+    (70, 1, q4.MAX_ROUTED, 16, 64, np.float16),          # the most experts per row
+    (q4.MAX_EXPERTS, 2, 8, 16, 32, np.float32),          # the largest stack
+    (300, 64, 64, 16, 32, np.float32),                   # 4096 pairs: the by-expert limit
+], ids=["one-expert", "k64", "4096-experts", "4096-pairs"])
+def test_routed_limits(rk, n_exp, n, k, out, in_, xdt):
+    blks, stack = _expert_stack(n_exp, out, in_, seed=140)
+    x = synth.make_x(n, in_, seed=141, dtype=xdt)
+    route = np.random.default_rng(142).integers(0, n_exp, size=(n, k)).astype(np.int32)
+    yy = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out,
+                          route_kernel=rk).cpu().numpy()
+    worst = 0.0
+    for t in range(n):
+        for j in range(k):
+            p, e = t * k + j, int(route[t, j])
+            y_ref, den = oracle.matmul(blks[e], x[t:t + 1], out, in_)
+            worst = max(worst, oracle.max_ratio(yy[p:p + 1], y_ref, den))
+    assert worst <= TOL_SMALL_N
