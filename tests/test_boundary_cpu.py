@@ -46,6 +46,10 @@ def test_header_constants_match_binding():
     assert consts["KERNEL_GEMM"] == q4.KERNEL_GEMM
     assert consts["MAX_IN"] == q4.MAX_IN and consts["MAX_OUT"] == q4.MAX_OUT
     assert consts["MAX_N"] == q4.MAX_N
+    assert consts["MAX_EXPERTS"] == q4.MAX_EXPERTS and consts["MAX_ROUTED"] == q4.MAX_ROUTED
+    assert consts["ROUTE_AUTO"] == q4.ROUTE_AUTO
+    assert consts["ROUTE_BY_COLUMN"] == q4.ROUTE_BY_COLUMN
+    assert consts["ROUTE_BY_EXPERT"] == q4.ROUTE_BY_EXPERT
 
 
 @pytest.mark.parametrize("out,in_", [(1024, 1024), (9728, 2560), (151936, 2560),
