@@ -255,11 +255,13 @@ def decode_line(torch, q4, synth, name, linears, n, kernel, steps, warmup, group
     return res
 
 
-def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_=2048):
+def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_=2048,
+                hot=0):
     """Routed (mixture-of-experts) decode, synthetic: n rows of x, each through
     k distinct experts drawn from n_exp experts of out x in (an expert FFN
     projection of a mid-size mixture model; the experts' shape is chosen, not
-    taken from a page).  One q4_0_matmul_routed call per step, timed by
+    taken from a page), or with hot > 0 from the same first `hot` experts
+    (concentrated routing).  One q4_0_matmul_routed call per step, timed by
     column, by expert and as AUTO picks, and for n <= 4 against the same pairs
     as n*k single-row q4_0_matmul calls.  GB/s counts the distinct experts'
     Q4_0 bytes of a step."""
@@ -275,7 +277,8 @@ def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_
     stacks = [base] + [base.clone() for _ in range(copies - 1)]
     x = torch.from_numpy(synth.make_x(n, in_, seed=501)).cuda()
     rng = np.random.default_rng(502)
-    route_np = np.stack([rng.permutation(n_exp)[:k] for _ in range(n)]).astype(np.int32)
+    pool = hot if hot else n_exp
+    route_np = np.stack([rng.permutation(pool)[:k] for _ in range(n)]).astype(np.int32)
     route = torch.from_numpy(route_np).cuda()
     y = torch.empty((n * k, out), dtype=torch.float32, device="cuda")
     uniq = len(np.unique(route_np))
@@ -303,7 +306,8 @@ def routed_line(torch, q4, synth, n, steps, warmup, n_exp=128, k=8, out=768, in_
             ms[name] = None
     best = ms["by_column" if auto == q4.ROUTE_BY_COLUMN else "by_expert"]
     gbs = uniq * eb / (best * 1e-3) / 1e9
-    res = {"workload": "moe_routed_decode", "n": n, "experts": n_exp, "k": k,
+    res = {"workload": "moe_routed_decode" + (f"_hot{hot}" if hot else ""), "n": n,
+           "experts": n_exp, "k": k,
            "expert_shape": [out, in_], "distinct_experts": uniq,
            "auto": "by_column" if auto == q4.ROUTE_BY_COLUMN else "by_expert",
            "ms_per_step": round(best, 5), "steps": done,
@@ -479,6 +483,8 @@ def main():
                             w4a8=True)]
             extra["routed"] = [routed_line(torch, q4, synth, nn, 300, 20)
                                for nn in (1, 4, 16, 64)]
+            extra["routed"] += [routed_line(torch, q4, synth, nn, 300, 20, hot=16)
+                                for nn in (16, 64)]
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)
 
     if args.calib_copy:
