@@ -482,7 +482,7 @@ def main():
                 decode_line(torch, q4, synth, "logit_head", [(151936, 2560)], 1, 0, 200, 20,
                             w4a8=True)]
             extra["routed"] = [routed_line(torch, q4, synth, nn, 300, 20)
-                               for nn in (1, 4, 16, 64)]
+                               for nn in (1, 4, 16, 32, 64)]
             extra["routed"] += [routed_line(torch, q4, synth, nn, 300, 20, hot=16)
                                 for nn in (16, 64)]
             extra["prefill"] = prefill_line(torch, q4, synth, 0, 200, 20)

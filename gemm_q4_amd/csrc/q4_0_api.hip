@@ -74,10 +74,10 @@ constexpr int64_t kSmallNMax = 64;
 // matrices it was routed to, a prompt reads each expert once for the columns
 // that chose it, the two crossing near thirty-two columns): by expert from
 // this many x rows, by column below.  Measured on MI355X (128 experts of 768 x
-// 2048, 8 per row, graph replay), by column against by expert: n = 1 4.7 /
-// 12.9 us, n = 8 14.9 / 19.3, n = 16 27.7 / 26.7, n = 24 38.4 / 28.9, n = 32
-// 48.5 / 29.0, n = 64 87.9 / 36.2: the crossover sits at 16 rows on this part.
-constexpr int64_t kByExpertMinN = 16;
+// 2048, 8 per row, graph replay), by column against by expert: n = 4 8.1 /
+// 14.5 us, n = 8 14.6 / 19.1, n = 16 22.6 / 26.2, n = 24 33.3 / 28.4, n = 32
+// 39.6 / 29.1, n = 64 69.7 / 36.6: the crossover sits near 24 rows on this part.
+constexpr int64_t kByExpertMinN = 24;
 int auto_kernel(int64_t n, int64_t out, int64_t in, int x_f16) {
     if (n <= kSmallNMax && q4::gemv_mfma_supports(n, out, in, x_f16))
         return Q4_0_KERNEL_GEMV_MFMA;

@@ -1177,10 +1177,12 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         const GemvProblem &pr = probs[i];
         MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
         const Layout L(pr.out, pr.in);
-        if (by_expert) {
-            // about kMfmaTargetWgs workgroups over all chunks: each chunk's x
-            // fragments are loaded once per workgroup, so a chunk takes few
-            // workgroups with long runs of tiles
+        if (route) {
+            // about kMfmaTargetWgs workgroups over all pairs (chunks): each
+            // workgroup stages or loads its pair's (chunk's) x once, so with
+            // many pairs a pair takes few workgroups with long runs of tiles
+            // (by column at 16 rows: 22.3 us against 27.4 us with the
+            // one-linear plan's 48 workgroups per pair)
             int64_t gx = kMfmaTargetWgs / npairs_routed;
             if (gx < 1) gx = 1;
             if (gx > L.tiles) gx = L.tiles;

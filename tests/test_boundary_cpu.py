@@ -278,8 +278,8 @@ def test_routed_ex_and_route_choice():
                      0) == q4.EUNSUPPORTED
     sel = q4._lib.q4_0_select_route
     assert sel(1, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
-    assert sel(8, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
-    assert sel(16, 8, 128, 768, 2048) == q4.ROUTE_BY_EXPERT
+    assert sel(16, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
+    assert sel(24, 8, 128, 768, 2048) == q4.ROUTE_BY_EXPERT
     assert sel(65, 64, 128, 768, 2048) == q4.ROUTE_BY_COLUMN    # too many pairs by expert
     assert sel(1, 0, 128, 768, 2048) == q4.EINVAL
     assert sel(1, 8, 128, 768, 48) == q4.ESHAPE
