@@ -7,6 +7,19 @@ CPU-baseline leg may import this package.  It shares no code with the GPU
 library in ``gemm_q4_amd`` and neither imports the other.
 
 The C file's header states what the oracle follows and how it is pinned.
+The Python helpers here are pinned as follows (tests/test_oracle_pins.py;
+tests/test_oracle_mutants.py plants a mistake in each and checks that a pin
+fails):
+
+- max_ratio: hand-worked cases (a per-output ratio that a norm-wise ratio
+  would under-report, the absolute value, den = 0 with y = 0 and y != 0,
+  NaN and Inf outputs, all-zero inputs, the maximum over rows) and a plain
+  loop over the outputs on random data;
+- greedy_pick: hand-worked ties, NaN and all-NaN rows, and a brute-force
+  scan on random integer logits;
+- pick_within_tolerance: a near tie inside the two outputs' error budget,
+  a far value and an invalid index outside it, and a case that only a
+  two-sided budget accepts.
 """
 from __future__ import annotations
 

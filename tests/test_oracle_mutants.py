@@ -7,6 +7,12 @@ dropped last term, transposed activation or output indexing, a wrong
 binary16 exponent bias or subnormal scale, a signed magnitude sum; in the
 W4A8 part, ties rounded away from zero, a 255 instead of a 127 scale, a
 signed maximum, a dropped offset, the first block's activation scale.
+
+The oracle's Python helpers get their own planted mistakes (PY_MUTANTS):
+the acceptance ratio taken norm-wise, as a mean, against |y_ref|, without
+the absolute value, without the den = 0 or the non-finite rule; the greedy
+pick keeping the last of equal values or letting NaN win; the pick's
+tolerance test with a one-sided budget or none.
 """
 import os
 import tempfile
@@ -17,7 +23,8 @@ import pytest
 import oracle
 from oracle import build as obuild
 import synth
-from test_oracle_pins import (GOLDEN_CASES, _brute_w4a8, _golden_blocks, brute_force)
+from test_oracle_pins import (GOLDEN_CASES, _brute_w4a8, _golden_blocks, brute_force,
+                              ratio_battery)
 
 SRC = open(obuild.SRC).read()
 
@@ -128,3 +135,134 @@ def test_planted_mistake_is_caught(name):
         lib = obuild.build(src=src, lib=os.path.join(tmp, "libmut.so"))
         failed = battery(oracle.Oracle(lib))
     assert failed, f"mutant {name} passed every pin"
+
+
+# ---- planted mistakes in the oracle's Python helpers ----------------------
+def _ratio_norm_wise(y, y_ref, den):
+    """max |err| / max den (a norm-wise ratio)"""
+    return float(np.max(np.abs(y - y_ref)) / np.max(den))
+
+
+def _ratio_mean(y, y_ref, den):
+    nz = den != 0
+    if np.any(~nz & (y != 0)) or not np.all(np.isfinite(y[nz])):
+        return float("inf")
+    return float(np.mean(np.abs(y - y_ref)[nz] / den[nz])) if nz.any() else 0.0
+
+
+def _ratio_vs_ref(y, y_ref, den):
+    nz = den != 0
+    if np.any(~nz & (y != 0)) or not np.all(np.isfinite(y[nz])):
+        return float("inf")
+    return float(np.max(np.abs(y - y_ref)[nz] / np.abs(y_ref[nz]))) if nz.any() else 0.0
+
+
+def _ratio_signed(y, y_ref, den):
+    nz = den != 0
+    if np.any(~nz & (y != 0)) or not np.all(np.isfinite(y[nz])):
+        return float("inf")
+    return float(np.max((y - y_ref)[nz] / den[nz])) if nz.any() else 0.0
+
+
+def _ratio_no_zero_rule(y, y_ref, den):
+    nz = den != 0
+    if not np.all(np.isfinite(y[nz])):
+        return float("inf")
+    return float(np.max(np.abs(y - y_ref)[nz] / den[nz])) if nz.any() else 0.0
+
+
+def _ratio_nan_ignored(y, y_ref, den):
+    nz = den != 0
+    if np.any(~nz & (y != 0)):
+        return float("inf")
+    return float(np.nanmax(np.abs(y - y_ref)[nz] / den[nz])) if nz.any() else 0.0
+
+
+def _pick_last_of_ties(y_ref):
+    vals, idxs = [], []
+    for row in np.asarray(y_ref, np.float64):
+        best, bi = -np.inf, -1
+        for i, v in enumerate(row.tolist()):
+            if v >= best and not np.isnan(v):
+                best, bi = v, i
+        vals.append(best if bi >= 0 else np.nan)
+        idxs.append(bi)
+    return np.array(vals), np.array(idxs)
+
+
+def _pick_nan_wins(y_ref):
+    vals, idxs = [], []
+    for row in np.asarray(y_ref, np.float64):
+        i = int(np.argmax(row))           # numpy's argmax returns the first NaN
+        vals.append(row[i])
+        idxs.append(i)
+    return np.array(vals), np.array(idxs)
+
+
+def _pick_battery(pick):
+    y = np.array([[1.0, 3.0, 3.0, -2.0],
+                  [np.nan, -1.0, -1.0, -5.0],
+                  [np.nan, np.nan, np.nan, np.nan],
+                  [-np.inf, -np.inf, -7.0, -np.inf]])
+    v, i = pick(y)
+    ok = (list(i) == [1, 1, -1, 2] and v[0] == 3.0 and v[1] == -1.0 and np.isnan(v[2])
+          and v[3] == -7.0)
+    return [] if ok else ["pick"]
+
+
+def _within_one_sided(y_ref, den, idx, tol):
+    best, bi = oracle.greedy_pick(y_ref)
+    for t, i in enumerate(np.asarray(idx).tolist()):
+        if i < 0 or i >= y_ref.shape[1]:
+            return False
+        if y_ref[t, i] < best[t] - tol * den[t, bi[t]]:
+            return False
+    return True
+
+
+def _within_exact(y_ref, den, idx, tol):
+    _, bi = oracle.greedy_pick(y_ref)
+    return bool(np.all(np.asarray(idx) == bi))
+
+
+def _within_battery(within):
+    failed = []
+    y = np.array([[1.0, 1.0 - 1e-9, 0.5]])
+    den = np.full_like(y, 10.0)
+    if not (within(y, den, np.array([0]), 1e-3) and within(y, den, np.array([1]), 1e-3)):
+        failed.append("near_tie")
+    if within(y, den, np.array([2]), 1e-3) or within(y, den, np.array([-1]), 1e-3):
+        failed.append("far")
+    # the budget is both outputs' errors: 1.5e-3 below the maximum, dens 1 and 1
+    # (1e-3 each): inside 2e-3, outside a one-sided 1e-3
+    y2 = np.array([[1.0, 1.0 - 1.5e-3]])
+    if not within(y2, np.ones_like(y2), np.array([1]), 1e-3):
+        failed.append("two_sided")
+    return failed
+
+
+PY_MUTANTS = {
+    "ratio_norm_wise": ("max_ratio", _ratio_norm_wise),
+    "ratio_mean": ("max_ratio", _ratio_mean),
+    "ratio_vs_ref": ("max_ratio", _ratio_vs_ref),
+    "ratio_signed": ("max_ratio", _ratio_signed),
+    "ratio_no_zero_rule": ("max_ratio", _ratio_no_zero_rule),
+    "ratio_nan_ignored": ("max_ratio", _ratio_nan_ignored),
+    "pick_last_of_ties": ("greedy_pick", _pick_last_of_ties),
+    "pick_nan_wins": ("greedy_pick", _pick_nan_wins),
+    "within_one_sided": ("pick_within_tolerance", _within_one_sided),
+    "within_exact": ("pick_within_tolerance", _within_exact),
+}
+PY_BATTERY = {"max_ratio": ratio_battery, "greedy_pick": _pick_battery,
+              "pick_within_tolerance": _within_battery}
+
+
+@pytest.mark.parametrize("fn", sorted(PY_BATTERY))
+def test_unmutated_helpers_pass_battery(fn):
+    assert PY_BATTERY[fn](getattr(oracle, fn)) == []
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_planted_helper_mistake_is_caught(name):
+    fn, mutant = PY_MUTANTS[name]
+    assert PY_BATTERY[fn](mutant), f"mutant {name} of {fn} passed every pin"

@@ -346,6 +346,70 @@ def test_pick_within_tolerance_accepts_near_ties_only():
     assert not oracle.pick_within_tolerance(y, den, np.array([-1]), 1e-3)
 
 
+# ------------------------------------------------- the acceptance ratio
+# The tolerance of the product's contract is per output: |y - y_ref| divided
+# by that output's own sum of |w x|, maximised over every (row, output) pair;
+# an output whose every product is zero must come out exactly zero.  Each
+# case below is worked by hand and names what a plausible mistake in
+# max_ratio would change.
+RATIO_CASES = [
+    # (name, y, y_ref, den, expected)
+    # per-output, not norm-wise: 0.5 / 1 = 0.5; max|err| / max(den) = 0.005
+    ("per_output", [[1.5, 100.0]], [[1.0, 100.0]], [[1.0, 100.0]], 0.5),
+    # the ratio of a small error on a small den beats a large error on a
+    # large den: max(1/100, 0.1/0.1) = 1; max|err| / den(argmax err) = 0.01
+    ("small_den_wins", [[101.0, 0.2]], [[100.0, 0.1]], [[100.0, 0.1]], 1.0),
+    # absolute value: y below y_ref counts the same
+    ("below_ref", [[1.5]], [[2.0]], [[1.0]], 0.5),
+    # den = 0 with y = 0 is ignored; the other output decides: 0.5 / 2
+    ("zero_den_zero_y", [[0.0, 1.5]], [[0.0, 1.0]], [[0.0, 2.0]], 0.25),
+    # den = 0 with y != 0, however small: infinite
+    ("zero_den_nonzero_y", [[1e-30, 1.0]], [[0.0, 1.0]], [[0.0, 1.0]], float("inf")),
+    # a NaN or an infinity where den > 0: infinite
+    ("nan_y", [[float("nan"), 1.0]], [[0.0, 1.0]], [[1.0, 1.0]], float("inf")),
+    ("inf_y", [[1.0, float("inf")]], [[1.0, 1.0]], [[1.0, 1.0]], float("inf")),
+    # every den 0 and every y 0: nothing to compare, 0
+    ("all_zero", [[0.0, 0.0], [0.0, 0.0]], [[0.0, 0.0], [0.0, 0.0]],
+     [[0.0, 0.0], [0.0, 0.0]], 0.0),
+    # maximum over rows and outputs, each error against its own den:
+    # errors [[0.1, 0.2], [0.3, 0.0]], dens [[1, 4], [2, 1]] -> 0.15
+    ("two_rows", [[1.1, 2.2], [3.3, 4.0]], [[1.0, 2.0], [3.0, 4.0]],
+     [[1.0, 4.0], [2.0, 1.0]], 0.15),
+]
+
+
+def ratio_battery(fn):
+    """Names of the hand-worked cases on which fn(y, y_ref, den) is wrong."""
+    failed = []
+    for name, y, y_ref, den, expect in RATIO_CASES:
+        got = fn(np.array(y, np.float64), np.array(y_ref, np.float64),
+                 np.array(den, np.float64))
+        if expect == float("inf"):
+            ok = got == float("inf")
+        else:
+            ok = abs(got - expect) <= 1e-12 * max(1.0, expect)
+        if not ok:
+            failed.append(name)
+    return failed
+
+
+def test_max_ratio_hand_worked_cases():
+    assert ratio_battery(oracle.max_ratio) == []
+
+
+def test_max_ratio_is_the_per_output_maximum_on_random_data():
+    """On random data the ratio equals a plain loop over the outputs."""
+    rng = np.random.default_rng(11)
+    y_ref = rng.standard_normal((3, 40))
+    den = np.abs(rng.standard_normal((3, 40))) + 0.01
+    y = y_ref + rng.standard_normal((3, 40)) * 1e-4
+    expect = 0.0
+    for t in range(3):
+        for o in range(40):
+            expect = max(expect, abs(y[t, o] - y_ref[t, o]) / den[t, o])
+    assert oracle.max_ratio(y, y_ref, den) == expect
+
+
 # ------------------------------------------------------------------- W4A8
 def test_quantize_x8_hand_worked_block():
     """amax 127 gives d = 1 exactly, so the codes are x rounded to nearest,
