@@ -30,11 +30,11 @@
 //      value is exact q - 8 times d, rounded once to binary16.
 //   D: lane l holds weight row l%32 and activation rows 8(i/4) + 4h + i%4.
 //
-// Work split: whole 128 x 128 tiles for every full pass over the 256 compute
-// units; the tiles of the last, partial pass are cut along K into slices
+// Work split: whole 128 x 128 tiles for every full pass over the compute
+// units (256 on MI355X); the tiles of the last, partial pass are cut along K into slices
 // that spread over all compute units, their partial tiles parked in a
 // workspace and added in slice order by a second kernel (deterministic).
-// Consecutive workgroup ids are dealt to the eight dies in turn; the ids are
+// Consecutive workgroup ids are dealt to the dies (eight) in turn; the ids are
 // permuted so that each die takes a contiguous run of tiles in which the M
 // blocks of one N block are adjacent, and its L2 serves their shared words.
 #include <type_traits>
@@ -63,8 +63,6 @@ constexpr int kTileStride = 136;                  // epilogue tile row, floats
 constexpr int kEpiBytes = kGemmBM * kTileStride * 4;   // 68 KB
 constexpr int kGemmLds = kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
 static_assert(kGemmLds <= 160 * 1024, "LDS of one workgroup");
-constexpr int kDies = 8;
-constexpr int kComputeUnits = 256;
 
 struct GemmArgs {
     const uint8_t *packed;
@@ -77,6 +75,7 @@ struct GemmArgs {
     int nm, nn;           // M blocks, N blocks (tile t: M block t % nm, N block t / nm)
     int full;             // tiles 0 .. full-1 are computed whole
     int rem, split, gps;  // the rem other tiles: split K slices of gps groups each
+    int dies;             // dies (L2 domains) the ids are dealt over
     int die_full, die_split;  // permute ids per die in each part
 };
 
@@ -123,13 +122,13 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     const int id = blockIdx.x;
     int tile, gs0, gs1, piece = -1;
     if (id < a.full) {
-        tile = a.die_full ? (id % kDies) * (a.full / kDies) + id / kDies : id;
+        tile = a.die_full ? (id % a.dies) * (a.full / a.dies) + id / a.dies : id;
         gs0 = 0;
         gs1 = a.g4;
     } else {
         const int np = a.rem * a.split;
         int q = id - a.full;
-        if (a.die_split) q = (q % kDies) * (np / kDies) + q / kDies;
+        if (a.die_split) q = (q % a.dies) * (np / a.dies) + q / a.dies;
         piece = q;
         tile = a.full + q % a.rem;
         gs0 = (q / a.rem) * a.gps;
@@ -547,10 +546,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restric
     }
 }
 
-// Work split: whole tiles for as many full passes over the compute units as
-// the tile count allows; the remaining tiles (a partial pass) are cut along K
-// into as many slices as spread them over the compute units, each slice at
-// least kMinSliceGroups groups, and a second kernel adds the slices.
+// Work split: whole tiles for as many full passes over the device's compute
+// units as the tile count allows; the remaining tiles (a partial pass) are
+// cut along K into as many slices as spread them over the compute units, each
+// slice at least kMinSliceGroups groups, and a second kernel adds the slices.
 constexpr int kMinSliceGroups = 4;
 struct GemmPlan {
     int nm, nn, full, rem, split, gps;
@@ -559,12 +558,13 @@ struct GemmPlan {
 
 static GemmPlan gemm_plan(int64_t n, int64_t out, int64_t in) {
     const Layout L(out, in);
+    const int64_t cus = device_shape().cus;
     GemmPlan p;
     p.nm = (int)((n + kGemmBM - 1) / kGemmBM);
     p.nn = (int)((out + kGemmBN - 1) / kGemmBN);
     const int64_t tiles = (int64_t)p.nm * p.nn;
-    const int64_t rem = tiles % kComputeUnits;
-    int64_t split = rem > 0 ? kComputeUnits / rem : 1;
+    const int64_t rem = tiles % cus;
+    int64_t split = rem > 0 ? cus / rem : 1;
     const int64_t max_split = L.g4 / kMinSliceGroups;
     if (split > max_split) split = max_split;
     if (split < 2) {
@@ -616,8 +616,9 @@ hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y, i
     a.rem = p.rem;
     a.split = p.split;
     a.gps = p.gps;
-    a.die_full = (p.full > 0 && p.full % kDies == 0) ? 1 : 0;
-    a.die_split = (p.rem > 0 && (p.rem * p.split) % kDies == 0) ? 1 : 0;
+    a.dies = device_shape().dies;
+    a.die_full = (p.full > 0 && p.full % a.dies == 0) ? 1 : 0;
+    a.die_split = (p.rem > 0 && (p.rem * p.split) % a.dies == 0) ? 1 : 0;
     const dim3 grid((unsigned)p.wgs), block(kGemmWaves * 64);
     const size_t lds = (size_t)kGemmLds;
     if (x_f16)

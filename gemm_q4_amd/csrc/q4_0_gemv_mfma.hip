@@ -58,19 +58,20 @@
 
 namespace q4 {
 
-// Workgroups a launch aims for.  Each workgroup stages (or, from kPrepMinN
-// rows on, loads as prepared fragments) the x of its whole K range once and
-// walks a run of tiles with it; from four rows on those fragments outweigh
-// one 16-row tile's weights, so short runs multiply the traffic.  Measured on
-// MI355X (graph replay): up to a few thousand tile-slices about one workgroup
-// per compute unit is best (FFN-up 9728 x 2560, n = 1/4/8: 6.0/8.8/10.1 us
-// against 6.3/9.9/11.3 us with one tile per workgroup); the 151936-row logit
-// head wants about four per compute unit (39 us against 44 us).
-#ifndef Q4_MFMA_TARGET_WGS
-#define Q4_MFMA_TARGET_WGS 1024
+// Workgroups a launch aims for, per compute unit of the device.  Each
+// workgroup stages (or, from kPrepMinN rows on, loads as prepared fragments)
+// the x of its whole K range once and walks a run of tiles with it; from four
+// rows on those fragments outweigh one 16-row tile's weights, so short runs
+// multiply the traffic.  Measured on MI355X (256 compute units, graph
+// replay): up to a few thousand tile-slices about one workgroup per compute
+// unit is best (FFN-up 9728 x 2560, n = 1/4/8: 6.0/8.8/10.1 us against
+// 6.3/9.9/11.3 us with one tile per workgroup); the 151936-row logit head
+// wants about four per compute unit (39 us against 44 us).
+#ifndef Q4_MFMA_WGS_PER_CU
+#define Q4_MFMA_WGS_PER_CU 4
 #endif
-#ifndef Q4_MFMA_TARGET_WGS_SMALL
-#define Q4_MFMA_TARGET_WGS_SMALL 256
+#ifndef Q4_MFMA_WGS_PER_CU_SMALL
+#define Q4_MFMA_WGS_PER_CU_SMALL 1
 #endif
 #ifndef Q4_MFMA_MANY_TILES
 #define Q4_MFMA_MANY_TILES 4096
@@ -100,8 +101,11 @@ static int64_t slots_for(int64_t n) {
     n = kernel_rows(n);
     return n <= 8 ? 2 * n : n;
 }
-constexpr int kMfmaTargetWgs = Q4_MFMA_TARGET_WGS;
-constexpr int kMfmaTargetWgsSmall = Q4_MFMA_TARGET_WGS_SMALL;
+// workgroups a launch aims for on this device: many tiles, fewer tiles
+static int64_t target_wgs() { return (int64_t)device_shape().cus * Q4_MFMA_WGS_PER_CU; }
+static int64_t target_wgs_small() {
+    return (int64_t)device_shape().cus * Q4_MFMA_WGS_PER_CU_SMALL;
+}
 constexpr int64_t kMfmaManyTiles = Q4_MFMA_MANY_TILES;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
 // x items (8 values each) a lane holds while it stages: caps groups per wave x n
@@ -990,10 +994,10 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
     p.per = (int)((p.gps + waves - 1) / waves);
     p.waves = (int)((p.gps + p.per - 1) / p.per);
     p.gpw = gpw_for(p.per, n, prep);
-    // about kMfmaTargetWgs (or, for fewer tile-slices, kMfmaTargetWgsSmall)
+    // about target_wgs() (or, for fewer tile-slices, target_wgs_small())
     // workgroups in all, each walking a run of tiles
     const int64_t units = L.tiles * p.slices;
-    const int64_t target = units >= kMfmaManyTiles ? kMfmaTargetWgs : kMfmaTargetWgsSmall;
+    const int64_t target = units >= kMfmaManyTiles ? target_wgs() : target_wgs_small();
     int64_t tpw = (units + target - 1) / target;
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
@@ -1116,11 +1120,6 @@ bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n) {
     return true;
 }
 
-int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in) {
-    const MfmaPlan p = mfma_plan(n, out, in);
-    return p.gx * p.slices;
-}
-
 // Launches the instance if it exists (its groups fit the registers); returns
 // whether it did.
 template <int NT, typename XT, int GPW, bool PREP>
@@ -1178,12 +1177,12 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
         const Layout L(pr.out, pr.in);
         if (route) {
-            // about kMfmaTargetWgs workgroups over all pairs (chunks): each
+            // about target_wgs() workgroups over all pairs (chunks): each
             // workgroup stages or loads its pair's (chunk's) x once, so with
             // many pairs a pair takes few workgroups with long runs of tiles
             // (by column at 16 rows: 22.3 us against 27.4 us with the
             // one-linear plan's 48 workgroups per pair)
-            int64_t gx = kMfmaTargetWgs / npairs_routed;
+            int64_t gx = target_wgs() / npairs_routed;
             if (gx < 1) gx = 1;
             if (gx > L.tiles) gx = L.tiles;
             p.tpw = (L.tiles + gx - 1) / gx;

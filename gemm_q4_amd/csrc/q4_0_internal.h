@@ -17,10 +17,20 @@ inline int64_t grid_for(int64_t total, int block) {
     return g < 1 ? 1 : (g > cap ? cap : g);
 }
 
-// Workspace for kernels that split K across workgroups: per-slice partial
-// sums, written by the product kernel and read by the reduction kernel that
-// follows it on the same stream.
+// Largest workspace a call may need (the caller's buffer, Q4_0_WORKSPACE_MAX):
+// per-slice partial sums written by a product kernel and read by the
+// reduction kernel that follows it on the same stream, activations converted
+// by a pre-pass, routing tables.  Plans that would need more are unsupported.
 constexpr size_t kWorkspaceBytes = size_t(128) << 20;
+
+// Compute units and dies (XCDs) of the current HIP device, read once per
+// device with hipDeviceGetAttribute.  They set how work is split (and so the
+// workspace a call needs).  Without a visible device (size queries on a host
+// with no GPU) the MI355X's 256 and 8.
+struct DeviceShape {
+    int cus, dies;
+};
+DeviceShape device_shape();
 
 hipError_t launch_repack(const void *blocks, void *packed, int64_t out, int64_t in,
                          hipStream_t stream);
@@ -75,7 +85,6 @@ hipError_t launch_gemv_mfma_by_expert(const void *experts, int64_t n_experts, co
                                       int x_f16, const int32_t *route, int64_t k, float *y,
                                       int64_t n, int64_t out, int64_t in, void *ws,
                                       hipStream_t stream);
-int64_t gemv_mfma_workgroups(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemv_mfma(const void *packed, const void *x, int x_f16, float *y,
                             int64_t n, int64_t out, int64_t in, void *ws,
                             hipStream_t stream);
@@ -105,8 +114,11 @@ size_t gemm_workspace_bytes(int64_t n, int64_t out, int64_t in);
 hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y,
                        int64_t n, int64_t out, int64_t in, void *ws, hipStream_t stream);
 
-// Measurement aid: back-to-back v_mfma_f32_32x32x16_f16 on every SIMD.
+// Measurement aids: back-to-back v_mfma_f32_32x32x16_f16 on every SIMD; a
+// plain streaming read of `bytes` bytes (an empty launch for 0).
 int64_t mfma_loop_flops(int64_t workgroups, int64_t iters);
 hipError_t launch_mfma_loop(float *sink, int64_t workgroups, int64_t iters, hipStream_t stream);
+hipError_t launch_stream_read(const void *src, int64_t bytes, float *sink, int64_t workgroups,
+                              hipStream_t stream);
 
 }  // namespace q4

@@ -39,6 +39,9 @@ def test_header_constants_match_binding():
     assert consts["ESHAPE"] == q4.ESHAPE and consts["ENULL"] == q4.ENULL
     assert consts["EALIGN"] == q4.EALIGN and consts["EALIAS"] == q4.EALIAS
     assert consts["EUNSUPPORTED"] == q4.EUNSUPPORTED and consts["EHIP"] == q4.EHIP
+    assert consts["EWORKSPACE"] == q4.EWORKSPACE
+    assert consts["WORKSPACE_MAX"] == q4.WORKSPACE_MAX
+    assert consts["WORKSPACE_ALIGN"] == q4.WORKSPACE_ALIGN
     assert consts["F32"] == q4.F32 and consts["F16"] == q4.F16
     assert consts["KERNEL_AUTO"] == q4.KERNEL_AUTO
     assert consts["KERNEL_GEMV_DPP"] == q4.KERNEL_GEMV_DPP
@@ -105,20 +108,20 @@ def status_of(fn, *args):
     ((A16, B16, q4.F32, A16 + 16, 1, 10, 64), q4.EALIAS),    # y inside W
 ])
 def test_matmul_validation(args, expect):
-    assert status_of(q4.q4_0_matmul, *args, 0) == expect
+    assert status_of(q4.q4_0_matmul, *args) == expect
 
 
 def test_matmul_ex_rejects_bad_kernel_and_unsupported_shapes():
-    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, 9, 0) == q4.EINVAL
-    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, -1, 0) == q4.EINVAL
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, 9) == q4.EINVAL
+    assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 1, 10, 64, -1) == q4.EINVAL
     # the VALU kernel takes n <= 8, the small-n MFMA kernel n <= 64
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 9, 10, 64,
-                     q4.KERNEL_GEMV_DPP, 0) == q4.EUNSUPPORTED
+                     q4.KERNEL_GEMV_DPP) == q4.EUNSUPPORTED
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 65, 10, 64,
-                     q4.KERNEL_GEMV_MFMA, 0) == q4.EUNSUPPORTED
+                     q4.KERNEL_GEMV_MFMA) == q4.EUNSUPPORTED
     # the LDS-staged kernel cannot hold 8 rows of a 16384-wide x
     assert status_of(q4.q4_0_matmul_ex, A16, B16, q4.F32, C16, 8, 10, 16384,
-                     q4.KERNEL_GEMV_DPP, 0) == q4.EUNSUPPORTED
+                     q4.KERNEL_GEMV_DPP) == q4.EUNSUPPORTED
 
 
 @pytest.mark.parametrize("fn", [q4.q4_0_repack, q4.q4_0_unpack])
@@ -166,7 +169,7 @@ def test_kernel_supports():
 
 def test_strerror_covers_every_status():
     for st in (q4.OK, q4.EINVAL, q4.ESHAPE, q4.ENULL, q4.EALIGN, q4.EALIAS,
-               q4.EUNSUPPORTED, q4.EHIP):
+               q4.EUNSUPPORTED, q4.EHIP, q4.EWORKSPACE):
         assert q4.q4_0_strerror(st) != "unknown status"
     assert q4.q4_0_strerror(-99) == "unknown status"
     assert q4.q4_0_version() >= 100
@@ -198,16 +201,16 @@ def test_argmax_validation():
     am = q4.q4_0_matmul_argmax
     D16 = 1 << 38
     E16 = 1 << 39
-    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 48, D16, E16, 0) == q4.ESHAPE
-    assert status_of(am, A16, B16, 5, C16, 1, 10, 64, D16, E16, 0) == q4.EINVAL
-    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, 0, E16, 0) == q4.ENULL
-    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, D16, 0, 0) == q4.ENULL
-    assert status_of(am, 0, B16, q4.F32, C16, 1, 10, 64, D16, E16, 0) == q4.ENULL
-    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, D16 + 2, E16, 0) == q4.EALIGN
-    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, B16 + 4, E16, 0) == q4.EALIAS
-    assert status_of(am, A16, B16, q4.F32, C16, 2, 10, 64, D16, D16 + 4, 0) == q4.EALIAS
-    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, C16 + 8, E16, 0) == q4.EALIAS
-    assert status_of(am, A16, B16, q4.F32, C16, 65, 10, 64, D16, E16, 0) == q4.EUNSUPPORTED
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 48, D16, E16) == q4.ESHAPE
+    assert status_of(am, A16, B16, 5, C16, 1, 10, 64, D16, E16) == q4.EINVAL
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, 0, E16) == q4.ENULL
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, D16, 0) == q4.ENULL
+    assert status_of(am, 0, B16, q4.F32, C16, 1, 10, 64, D16, E16) == q4.ENULL
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, D16 + 2, E16) == q4.EALIGN
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, B16 + 4, E16) == q4.EALIAS
+    assert status_of(am, A16, B16, q4.F32, C16, 2, 10, 64, D16, D16 + 4) == q4.EALIAS
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 10, 64, C16 + 8, E16) == q4.EALIAS
+    assert status_of(am, A16, B16, q4.F32, C16, 65, 10, 64, D16, E16) == q4.EUNSUPPORTED
 
 
 def test_w4a8_validation():
@@ -219,21 +222,21 @@ def test_w4a8_validation():
     assert status_of(qx, A16, q4.F32, B16 + 4, C16, 1, 64, 0) == q4.EALIGN
     assert status_of(qx, A16, q4.F32, A16 + 16, C16, 1, 64, 0) == q4.EALIAS
     assert status_of(qx, A16, q4.F32, B16, B16 + 16, 1, 64, 0) == q4.EALIAS
-    assert status_of(mm, A16, B16, C16, D16, 1, 10, 48, 0) == q4.ESHAPE
-    assert status_of(mm, A16, 0, C16, D16, 1, 10, 64, 0) == q4.ENULL
-    assert status_of(mm, A16, B16 + 8, C16, D16, 1, 10, 64, 0) == q4.EALIGN
-    assert status_of(mm, A16, B16, C16, B16 + 32, 1, 10, 64, 0) == q4.EALIAS
-    assert status_of(mm, A16, B16, C16, A16 + 64, 1, 10, 64, 0) == q4.EALIAS
-    assert status_of(mm, A16, B16, C16, D16, 65, 10, 64, 0) == q4.EUNSUPPORTED
+    assert status_of(mm, A16, B16, C16, D16, 1, 10, 48) == q4.ESHAPE
+    assert status_of(mm, A16, 0, C16, D16, 1, 10, 64) == q4.ENULL
+    assert status_of(mm, A16, B16 + 8, C16, D16, 1, 10, 64) == q4.EALIGN
+    assert status_of(mm, A16, B16, C16, B16 + 32, 1, 10, 64) == q4.EALIAS
+    assert status_of(mm, A16, B16, C16, A16 + 64, 1, 10, 64) == q4.EALIAS
+    assert status_of(mm, A16, B16, C16, D16, 65, 10, 64) == q4.EUNSUPPORTED
 
 
 def test_mfma_loop_validation():
     f = q4.q4_0_mfma_loop
     assert status_of(f, 0, 1, 1, 0) == q4.ENULL
-    assert status_of(f, A16, 0, 1, 0) == q4.EINVAL
-    assert status_of(f, A16, 65537, 1, 0) == q4.EINVAL
-    assert status_of(f, A16, 1, 0, 0) == q4.EINVAL
-    assert status_of(f, A16, 1, 1000001, 0) == q4.EINVAL
+    assert status_of(f, A16, 0, 1) == q4.EINVAL
+    assert status_of(f, A16, 65537, 1) == q4.EINVAL
+    assert status_of(f, A16, 1, 0) == q4.EINVAL
+    assert status_of(f, A16, 1, 1000001) == q4.EINVAL
 
 
 def test_bench_refuses_more_than_one_gpu():
@@ -255,27 +258,27 @@ def test_routed_validation():
     D16 = 1 << 38
     E16 = 1 << 39
     # experts, n_experts, x, x_dtype, route, k, y, n, out, in
-    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, D16, 1, 10, 48, 0) == q4.ESHAPE
-    assert status_of(f, A16, 0, B16, q4.F32, C16, 2, D16, 1, 10, 64, 0) == q4.EINVAL
-    assert status_of(f, A16, 4, B16, q4.F32, C16, 0, D16, 1, 10, 64, 0) == q4.EINVAL
-    assert status_of(f, A16, 4, B16, q4.F32, C16, q4.MAX_ROUTED + 1, D16, 1, 10, 64, 0) == q4.EINVAL
-    assert status_of(f, A16, q4.MAX_EXPERTS + 1, B16, q4.F32, C16, 2, D16, 1, 10, 64, 0) == q4.EINVAL
-    assert status_of(f, A16, 4, B16, 7, C16, 2, D16, 1, 10, 64, 0) == q4.EINVAL
-    assert status_of(f, A16, 4, B16, q4.F32, 0, 2, D16, 1, 10, 64, 0) == q4.ENULL
-    assert status_of(f, A16 + 8, 4, B16, q4.F32, C16, 2, D16, 1, 10, 64, 0) == q4.EALIGN
-    assert status_of(f, A16, 4, B16, q4.F32, C16 + 2, 2, D16, 1, 10, 64, 0) == q4.EALIGN
-    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, B16 + 16, 1, 10, 64, 0) == q4.EALIAS
-    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, A16 + 64, 1, 10, 64, 0) == q4.EALIAS
-    assert status_of(f, A16, 4, B16, q4.F32, E16, 2, E16 - 64, 1, 10, 64, 0) == q4.EALIAS
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, D16, 1, 10, 48) == q4.ESHAPE
+    assert status_of(f, A16, 0, B16, q4.F32, C16, 2, D16, 1, 10, 64) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 0, D16, 1, 10, 64) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, C16, q4.MAX_ROUTED + 1, D16, 1, 10, 64) == q4.EINVAL
+    assert status_of(f, A16, q4.MAX_EXPERTS + 1, B16, q4.F32, C16, 2, D16, 1, 10, 64) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, 7, C16, 2, D16, 1, 10, 64) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, 0, 2, D16, 1, 10, 64) == q4.ENULL
+    assert status_of(f, A16 + 8, 4, B16, q4.F32, C16, 2, D16, 1, 10, 64) == q4.EALIGN
+    assert status_of(f, A16, 4, B16, q4.F32, C16 + 2, 2, D16, 1, 10, 64) == q4.EALIGN
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, B16 + 16, 1, 10, 64) == q4.EALIAS
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, A16 + 64, 1, 10, 64) == q4.EALIAS
+    assert status_of(f, A16, 4, B16, q4.F32, E16, 2, E16 - 64, 1, 10, 64) == q4.EALIAS
 
 
 def test_routed_ex_and_route_choice():
     D16 = 1 << 38
     f = q4.q4_0_matmul_routed_ex
-    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, D16, 1, 10, 64, 3, 0) == q4.EINVAL
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 2, D16, 1, 10, 64, 3) == q4.EINVAL
     # by expert takes at most 4096 pairs
-    assert status_of(f, A16, 4, B16, q4.F32, C16, 64, D16, 65, 10, 64, q4.ROUTE_BY_EXPERT,
-                     0) == q4.EUNSUPPORTED
+    assert status_of(f, A16, 4, B16, q4.F32, C16, 64, D16, 65, 10, 64,
+                     q4.ROUTE_BY_EXPERT) == q4.EUNSUPPORTED
     sel = q4._lib.q4_0_select_route
     assert sel(1, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
     assert sel(16, 8, 128, 768, 2048) == q4.ROUTE_BY_COLUMN
@@ -283,3 +286,89 @@ def test_routed_ex_and_route_choice():
     assert sel(65, 64, 128, 768, 2048) == q4.ROUTE_BY_COLUMN    # too many pairs by expert
     assert sel(1, 0, 128, 768, 2048) == q4.EINVAL
     assert sel(1, 8, 128, 768, 48) == q4.ESHAPE
+
+
+# ---- workspaces: sizes, and calls without enough of one -------------------
+W16 = 1 << 42      # a fake, 256-byte aligned workspace address
+
+
+def test_workspace_sizes_of_the_workloads():
+    """The headline decode call needs no workspace; the pre-pass (n >= 6),
+    the split K range of the prefill product and the greedy pick do."""
+    mws = q4.q4_0_matmul_workspace_size
+    assert mws(1, 9728, 2560) == 0
+    assert mws(1, 151936, 2560) == 0
+    assert 0 < mws(8, 9728, 2560) <= q4.WORKSPACE_MAX
+    assert 0 < mws(512, 9728, 2560, q4.F16) <= q4.WORKSPACE_MAX
+    assert mws(1, 9728, 2560, q4.F32, q4.KERNEL_GEMV_DPP) == 0
+    assert 0 < q4.q4_0_argmax_workspace_size(1, 151936, 2560) <= q4.WORKSPACE_MAX
+    assert q4.q4_0_routed_workspace_size(64, 8, 128, 768, 2048, q4.ROUTE_BY_EXPERT) > 0
+    assert q4.q4_0_w4a8_workspace_size(1, 9728, 2560) >= 0
+    lin = [(A16, B16, C16, 4096, 2560), (A16 + (1 << 24), B16, C16 + (1 << 24), 1024, 2560)]
+    g = q4.q4_0_grouped_workspace_size(lin, q4.F32, 8)
+    assert g >= max(mws(8, 4096, 2560), mws(8, 1024, 2560))
+    # an invalid shape or selector is reported as the call would report it
+    for bad, st in (((0, 10, 64), q4.ESHAPE), ((1, 10, 48), q4.ESHAPE)):
+        with pytest.raises(q4.Q4Error) as e:
+            mws(*bad)
+        assert e.value.status == st
+    with pytest.raises(q4.Q4Error) as e:
+        mws(65, 10, 64, q4.F32, q4.KERNEL_GEMV_MFMA)
+    assert e.value.status == q4.EUNSUPPORTED
+
+
+def test_calls_without_enough_workspace_are_refused():
+    need = q4.q4_0_matmul_workspace_size(8, 9728, 2560)
+    mm = q4.q4_0_matmul
+    args = (A16, B16, q4.F32, C16, 8, 9728, 2560)
+    assert status_of(mm, *args, None, 0) == q4.EWORKSPACE
+    assert status_of(mm, *args, W16, need - 1) == q4.EWORKSPACE
+    assert status_of(mm, *args, W16 + 128, need) == q4.EALIGN
+    assert status_of(mm, *args, B16 + 256, need) == q4.EALIAS     # inside x
+    assert status_of(mm, *args, C16 - 256, need) == q4.EALIAS     # runs into y
+    # prefill
+    need = q4.q4_0_matmul_workspace_size(512, 9728, 2560, q4.F16)
+    assert status_of(mm, A16, B16, q4.F16, C16, 512, 9728, 2560, None, 0) == q4.EWORKSPACE
+    assert status_of(mm, A16, B16, q4.F16, C16, 512, 9728, 2560, W16, need // 2) == \
+        q4.EWORKSPACE
+    # the greedy pick always needs one
+    D16, E16 = 1 << 38, 1 << 39
+    need = q4.q4_0_argmax_workspace_size(1, 1024, 1024)
+    am = q4.q4_0_matmul_argmax
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 1024, 1024, D16, E16) == q4.EWORKSPACE
+    assert status_of(am, A16, B16, q4.F32, C16, 1, 1024, 1024, D16, E16, D16,
+                     need) in (q4.EALIAS,)
+    # routed and grouped
+    need = q4.q4_0_routed_workspace_size(64, 8, 128, 768, 2048, q4.ROUTE_BY_EXPERT)
+    f = q4.q4_0_matmul_routed_ex
+    assert status_of(f, A16, 128, B16, q4.F32, C16, 8, D16, 64, 768, 2048,
+                     q4.ROUTE_BY_EXPERT, W16, need - 256) == q4.EWORKSPACE
+    lin = [(A16, B16, C16, 9728, 2560)]
+    assert status_of(q4.q4_0_matmul_grouped, lin, q4.F32, 8) == q4.EWORKSPACE
+
+
+def test_grouped_call_checks_every_linear_before_enqueuing():
+    """A group whose second linear no kernel can take fails with
+    EUNSUPPORTED before the first linear is enqueued (on this host, with no
+    GPU, any launch would fail with EHIP instead)."""
+    n = q4.MAX_N
+    ok = (A16, B16, C16, 64, 64)                                   # tiled product
+    big = (A16 + (1 << 24), B16, 1 << 45, 40000, 64)               # n * out > 2^31
+    ws = q4.WORKSPACE_MAX
+    assert status_of(q4.q4_0_matmul_grouped, [ok, big], q4.F32, n, W16, ws) == \
+        q4.EUNSUPPORTED
+    # a null pointer in the last linear: ENULL, nothing enqueued
+    assert status_of(q4.q4_0_matmul_grouped, [ok, (0, B16, 1 << 45, 64, 64)], q4.F32, 1,
+                     W16, ws) == q4.ENULL
+
+
+def test_stream_read_validation():
+    f = q4.q4_0_stream_read
+    assert status_of(f, A16, 16, 0, 1) == q4.ENULL                # no sink
+    assert status_of(f, 0, 16, B16, 1) == q4.ENULL                # bytes but no source
+    assert status_of(f, A16, 15, B16, 1) == q4.EINVAL             # not whole 16 bytes
+    assert status_of(f, A16, -16, B16, 1) == q4.EINVAL
+    assert status_of(f, A16, 16, B16, 0) == q4.EINVAL
+    assert status_of(f, A16, 16, B16, 65537) == q4.EINVAL
+    assert status_of(f, A16 + 4, 16, B16, 1) == q4.EALIGN
+    assert status_of(f, A16, 1 << 20, A16 + 64, 4) == q4.EALIAS
