@@ -71,6 +71,7 @@ KERNEL_NAMES = {KERNEL_AUTO: "auto", KERNEL_GEMV_DPP: "gemv_dpp",
 MAX_IN, MAX_OUT, MAX_N = 1048576, 16777216, 65536
 MAX_EXPERTS, MAX_ROUTED = 4096, 64
 WORKSPACE_MAX, WORKSPACE_ALIGN = 134217728, 256
+STATIC_SCRATCH_BYTES = 16777216
 ROUTE_AUTO, ROUTE_BY_COLUMN, ROUTE_BY_EXPERT = 0, 1, 2
 
 _i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -83,6 +84,7 @@ _SIGS = {
     "q4_0_matmul": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "q4_0_matmul_ex": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "q4_0_matmul_workspace_size": (_int, [_i64, _i64, _i64, _int, _int, _szp]),
+    "q4_0_matmul_static": (_int, [_vp, _vp, _int, _vp, _i64, _i64, _i64, _vp]),
     "q4_0_select_kernel": (_int, [_i64, _i64, _i64, _int]),
     "q4_0_kernel_supports": (_int, [_int, _i64, _i64, _i64, _int]),
     "q4_0_strerror": (ctypes.c_char_p, [_int]),
@@ -198,6 +200,12 @@ def q4_0_matmul_ex(packed, x, x_dtype: int, y, n: int, out: int, in_: int,
                                in_, kernel, _ptr(workspace),
                                _nbytes(workspace, workspace_bytes),
                                _stream(stream, packed, x, y)), "q4_0_matmul_ex")
+
+
+def q4_0_matmul_static(packed, x, x_dtype: int, y, n: int, out: int, in_: int,
+                       stream=None) -> None:
+    _check(_lib.q4_0_matmul_static(_ptr(packed), _ptr(x), x_dtype, _ptr(y), n, out, in_,
+                                   _stream(stream, packed, x, y)), "q4_0_matmul_static")
 
 
 def q4_0_matmul_workspace_size(n: int, out: int, in_: int, x_dtype: int = F32,

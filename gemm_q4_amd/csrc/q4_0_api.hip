@@ -9,8 +9,9 @@
 
 namespace q4 {
 
-namespace {
 constexpr int kMaxDevices = 64;
+
+namespace {
 std::mutex g_shape_mu;
 DeviceShape g_shape[kMaxDevices];
 bool g_shape_known[kMaxDevices];
@@ -46,6 +47,33 @@ DeviceShape device_shape() {
 }  // namespace q4
 
 namespace {
+
+// Scratch of q4_0_matmul_static: one array per GPU (each device holds its own
+// copy of a __device__ variable), alive until the process ends.  Host code
+// must not use the array's name as an address: the per-device address comes
+// from hipGetSymbolAddress, taken once per device on the first call there.
+static __device__ __align__(256) uint8_t scratch[Q4_0_STATIC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[q4::kMaxDevices];
+
+int scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= q4::kMaxDevices) {
+        (void)hipGetLastError();
+        return Q4_0_EHIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return Q4_0_EHIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return Q4_0_OK;
+}
 
 int check_shape(int64_t n, int64_t out, int64_t in) {
     if (n < 1 || n > Q4_0_MAX_N) return Q4_0_ESHAPE;
@@ -336,6 +364,28 @@ int q4_0_matmul(const void *packed, const void *x, int x_dtype, float *y, int64_
                 void *stream) {
     return q4_0_matmul_ex(packed, x, x_dtype, y, n, out, in, Q4_0_KERNEL_AUTO, workspace,
                           workspace_bytes, stream);
+}
+
+int q4_0_matmul_static(const void *packed, const void *x, int x_dtype, float *y, int64_t n,
+                       int64_t out, int64_t in, void *stream) {
+    // the checks of q4_0_matmul first (nothing is touched on an invalid call),
+    // then the scratch need against the static buffer
+    size_t need = 0;
+    const int st = check_shape(n, out, in);
+    if (st != Q4_0_OK) return st;
+    if (!valid_dtype(x_dtype)) return Q4_0_EINVAL;
+    if (!packed || !x || !y) return Q4_0_ENULL;
+    const int k = resolve_kernel(n, out, in, x_dtype, Q4_0_KERNEL_AUTO);
+    if (k < 0) return k;
+    need = kernel_workspace(k, n, out, in);
+    if (need > (size_t)Q4_0_STATIC_SCRATCH_BYTES) return Q4_0_EWORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int sst = scratch_address(&ws);
+        if (sst != Q4_0_OK) return sst;
+    }
+    return q4_0_matmul_ex(packed, x, x_dtype, y, n, out, in, Q4_0_KERNEL_AUTO, ws,
+                          need > 0 ? (size_t)Q4_0_STATIC_SCRATCH_BYTES : 0, stream);
 }
 
 int q4_0_argmax_workspace_size(int64_t n, int64_t out, int64_t in, int x_dtype,

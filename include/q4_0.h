@@ -155,6 +155,21 @@ int q4_0_matmul_ex(const void *packed, const void *x, int x_dtype, float *y,
                    int64_t n, int64_t out, int64_t in, int kernel,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory at all (code under HIP
+ * graph capture that may not allocate, tight serving loops, harnesses that
+ * forbid hipMalloc): q4_0_matmul with its scratch memory taken from a
+ * buffer of Q4_0_STATIC_SCRATCH_BYTES that the library holds in device
+ * memory, one per GPU, for the life of the process.  Arguments, results and
+ * errors as q4_0_matmul (the same kernels run); Q4_0_EWORKSPACE when the call
+ * would need more scratch than that (q4_0_matmul_workspace_size tells).
+ * Every call on a GPU shares that GPU's buffer: calls whose work overlaps
+ * in time on one GPU (different streams, concurrent graph replays) race and
+ * give wrong results; calls ordered on one stream are safe.  Nothing in the
+ * buffer needs to start at zero; it keeps the last call's contents. */
+#define Q4_0_STATIC_SCRATCH_BYTES 16777216
+int q4_0_matmul_static(const void *packed, const void *x, int x_dtype, float *y,
+                       int64_t n, int64_t out, int64_t in, void *stream);
+
 /* Workspace bytes of q4_0_matmul_ex with these sizes and kernel (AUTO: of
  * q4_0_matmul) into *bytes.  Host only.  Returns Q4_0_OK, or the status the
  * call itself would return for an invalid shape, dtype or selector, or
