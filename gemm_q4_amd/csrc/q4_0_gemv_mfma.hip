@@ -101,6 +101,16 @@ static int64_t slots_for(int64_t n) {
     n = kernel_rows(n);
     return n <= 8 ? 2 * n : n;
 }
+// A group of linears in one launch aims for this many workgroups per compute
+// unit over all its linears, each linear's share in proportion to its weight
+// bytes (tiles x groups per row, so a workgroup's run takes about as long in
+// every linear):
+// targets taken per linear would add up to several workgroups per compute
+// unit, each walking short runs of tiles and loading its K range of x (at
+// eight rows, 80-152 KB of prepared fragments) for each short run.
+#ifndef Q4_MFMA_GROUP_WGS_PER_CU
+#define Q4_MFMA_GROUP_WGS_PER_CU 1
+#endif
 // workgroups a launch aims for on this device: many tiles, fewer tiles
 static int64_t target_wgs() { return (int64_t)device_shape().cus * Q4_MFMA_WGS_PER_CU; }
 static int64_t target_wgs_small() {
@@ -381,11 +391,23 @@ __device__ __forceinline__ void xprep_row(const XT *__restrict__ x, int in, int 
     }
 }
 
+// The pre-pass of a launch: every distinct x of its linears, one workgroup
+// per (x, row), in one launch (a group of linears with different inputs,
+// e.g. every projection of a decoder block, needs one pre-pass launch, not
+// one per input).
+struct PrepSet {
+    const void *x[kMaxGroupLinears];
+    uint8_t *frag[kMaxGroupLinears];
+    int in[kMaxGroupLinears];
+    int nbpad[kMaxGroupLinears];
+    int count;
+    int rows;                 // rows of each x (workgroups per x)
+};
 template <int NT, typename XT>
-__global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const XT *__restrict__ x, int in,
-                                                             int nbpad, uint8_t *__restrict__ frag,
-                                                             const XRegions reg) {
-    xprep_row<NT, XT>(x, in, nbpad, frag, reg, (int)blockIdx.x);
+__global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const PrepSet set) {
+    const int e = (int)blockIdx.x / set.rows, t = (int)blockIdx.x - e * set.rows;
+    xprep_row<NT, XT>((const XT *)set.x[e], set.in[e], set.nbpad[e], set.frag[e], XRegions{},
+                      t);
 }
 
 // Routed by expert: the plan.  One workgroup (of kPlanThreads) buckets the pairs p = t*k + j by
@@ -1172,10 +1194,28 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
     const bool by_expert = route && route->chunk_expert;
     if (route && (by_expert ? (!prep || nrows != kChunkRows || NT != kChunkRows) : prep))
         return hipErrorInvalidValue;
+    // a group: the weight groups of all its linears, for the shared target
+    int64_t group_work = 0;
+    if (count > 1)
+        for (int i = 0; i < count; ++i) {
+            const Layout Li(probs[i].out, probs[i].in);
+            group_work += Li.tiles * Li.g4;
+        }
     for (int i = 0; i < count; ++i) {
         const GemvProblem &pr = probs[i];
         MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
         const Layout L(pr.out, pr.in);
+        if (count > 1) {
+            // this linear's share of the group's workgroups (the runs of
+            // tiles change, not the sums: a tile's waves and K slices are
+            // added in the same order whichever workgroup walks it)
+            const int64_t units = L.tiles * p.slices;
+            const int64_t total = (int64_t)device_shape().cus * Q4_MFMA_GROUP_WGS_PER_CU;
+            int64_t target = (total * L.tiles * L.g4 + group_work - 1) / group_work;
+            if (target < 1) target = 1;
+            p.tpw = (units + target - 1) / target;
+            p.gx = (L.tiles + p.tpw - 1) / p.tpw;
+        }
         if (route) {
             // about target_wgs() workgroups over all pairs (chunks): each
             // workgroup stages or loads its pair's (chunk's) x once, so with
@@ -1237,9 +1277,11 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         a.rt.part_pair = ra.part_pair;
         wg *= npairs_routed;
     }
-    // prepared launch: one pre-pass per distinct x of the group, its
-    // fragments after the partial sums in the workspace
+    // prepared launch: one pre-pass converting every distinct x of the group,
+    // each x's fragments after the partial sums in the workspace
     if (prep) {
+        PrepSet set = {};
+        set.rows = (int)nrows;
         for (int i = 0; i < count; ++i) {
             for (int j = 0; j < i && !a.lin[i].frag; ++j)
                 if (probs[j].x == probs[i].x && probs[j].in == probs[i].in)
@@ -1259,17 +1301,26 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             const int nbpad = a.lin[i].g4 * 4;
             // one workgroup per row of x (rows of the instance past nrows are
             // never read: their products land in outputs that are not stored)
-            if (by_expert)
+            if (by_expert) {
                 hipLaunchKernelGGL((route_prep_kernel<NT, XT>),
                                    dim3((unsigned)(1 + nrows * units)), dim3(kPrepThreads), 0,
                                    stream, route->route, route->x_rows * route->k,
                                    route->n_experts, (int)npairs_routed,
                                    (int32_t *)route->chunk_expert, (int32_t *)route->slot_pair,
                                    (const XT *)probs[i].x, (int)probs[i].in, nbpad, f, reg);
-            else
-                hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)(nrows * units)),
-                                   dim3(kPrepThreads), 0, stream, (const XT *)probs[i].x,
-                                   (int)probs[i].in, nbpad, f, reg);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            } else {
+                set.x[set.count] = probs[i].x;
+                set.frag[set.count] = f;
+                set.in[set.count] = (int)probs[i].in;
+                set.nbpad[set.count] = nbpad;
+                ++set.count;
+            }
+        }
+        if (set.count > 0) {
+            hipLaunchKernelGGL((xprep_kernel<NT, XT>), dim3((unsigned)(nrows * set.count)),
+                               dim3(kPrepThreads), 0, stream, set);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
