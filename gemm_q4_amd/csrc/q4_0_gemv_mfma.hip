@@ -66,9 +66,12 @@ namespace q4 {
 // replay): up to a few thousand tile-slices about one workgroup per compute
 // unit is best (FFN-up 9728 x 2560, n = 1/4/8: 6.0/8.8/10.1 us against
 // 6.3/9.9/11.3 us with one tile per workgroup); the 151936-row logit head
-// wants about four per compute unit (39 us against 44 us).
+// wants about two per compute unit (n = 1/4: 36.0/41.7 us against 36.7/43.7
+// us with four and 36.7/42.9 with three: at four rows its prepared instance
+// holds 158 VGPRs, three waves per SIMD, so four per compute unit left a
+// tail of workgroups that were not resident).
 #ifndef Q4_MFMA_WGS_PER_CU
-#define Q4_MFMA_WGS_PER_CU 4
+#define Q4_MFMA_WGS_PER_CU 2
 #endif
 #ifndef Q4_MFMA_WGS_PER_CU_SMALL
 #define Q4_MFMA_WGS_PER_CU_SMALL 1
