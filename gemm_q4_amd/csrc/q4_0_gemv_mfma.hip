@@ -114,6 +114,12 @@ static int64_t slots_for(int64_t n) {
 #ifndef Q4_MFMA_GROUP_WGS_PER_CU
 #define Q4_MFMA_GROUP_WGS_PER_CU 1
 #endif
+// Routed launches aim for this many workgroups per compute unit over all
+// their pairs or chunks (measured with 128 experts of 768 x 2048: about 1024
+// workgroups in all, 2048-8192 no better).
+#ifndef Q4_MFMA_ROUTED_WGS_PER_CU
+#define Q4_MFMA_ROUTED_WGS_PER_CU 4
+#endif
 // workgroups a launch aims for on this device: many tiles, fewer tiles
 static int64_t target_wgs() { return (int64_t)device_shape().cus * Q4_MFMA_WGS_PER_CU; }
 static int64_t target_wgs_small() {
@@ -1220,12 +1226,13 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
             p.gx = (L.tiles + p.tpw - 1) / p.tpw;
         }
         if (route) {
-            // about target_wgs() workgroups over all pairs (chunks): each
+            // about Q4_MFMA_ROUTED_WGS_PER_CU workgroups per compute unit over
+            // all pairs (chunks): each
             // workgroup stages or loads its pair's (chunk's) x once, so with
             // many pairs a pair takes few workgroups with long runs of tiles
             // (by column at 16 rows: 22.3 us against 27.4 us with the
             // one-linear plan's 48 workgroups per pair)
-            int64_t gx = target_wgs() / npairs_routed;
+            int64_t gx = (int64_t)device_shape().cus * Q4_MFMA_ROUTED_WGS_PER_CU / npairs_routed;
             if (gx < 1) gx = 1;
             if (gx > L.tiles) gx = L.tiles;
             p.tpw = (L.tiles + gx - 1) / gx;
