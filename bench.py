@@ -267,6 +267,25 @@ class Calibration:
         self.sink = torch.empty(65536, dtype=torch.float32, device="cuda")
         self.reads = {}
         self.floor = None
+        self.floor_isolated = None
+
+    def isolated_us(self, step, reps=200):
+        """Median time of one launch run alone: event, the launch, event,
+        then a synchronisation before the next (what a profiler's per-dispatch
+        duration measures, launch ramp included), in us."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        times = []
+        for i in range(reps + 10):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(i, stream.cuda_stream)
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 10:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        return round(float(np.median(times)), 3)
 
     def launch_floor_us(self, steps=500):
         if self.floor is None:
@@ -274,6 +293,8 @@ class Calibration:
             ms = time_steps(self.torch, lambda i, sh: q4.q4_0_stream_read(None, 0, sink, 256, sh),
                             steps, 20)
             self.floor = round(ms * 1e3, 3)
+            self.floor_isolated = self.isolated_us(
+                lambda i, sh: q4.q4_0_stream_read(None, 0, sink, 256, sh))
         return self.floor
 
     def read(self, nbytes, steps=200):
@@ -301,7 +322,7 @@ class Calibration:
         return res
 
     def summary(self):
-        return {"launch_floor_us": self.floor,
+        return {"launch_floor_us": self.floor, "launch_floor_isolated_us": self.floor_isolated,
                 "stream_read": sorted(self.reads.values(), key=lambda r: r["bytes"]),
                 "note": "empty launch and plain 16-byte non-temporal streaming read "
                         "(q4_0_stream_read), graph replay, weights rotated over >= 1 GiB"}
@@ -566,6 +587,13 @@ def main():
                    argmax=args.argmax, w4a8=args.w4a8)
         ms_eager = timed(torch, q4, cases, min(args.steps, 500), 5, graph=False,
                          groups=groups, argmax=args.argmax, w4a8=args.w4a8)
+        iso = None
+        if groups is None and not args.argmax and not args.w4a8 and len(cases) == 1:
+            c = cases[0]
+            ncp = len(c.packed)
+            iso = cal.isolated_us(lambda i, sh: q4.q4_0_matmul_ex(
+                c.packed[i % ncp], c.x, c.xcode, c.y, c.n, c.out, c.in_, c.kernel, c.ws,
+                c.ws_need, sh))
         parity = None if (args.argmax or args.w4a8) else max(
             parity_check(q4, __import__("oracle"), synth, c, seed=k) for k, c in enumerate(cases))
         value = total_w / (ms * 1e-3) / 1e9
@@ -583,6 +611,7 @@ def main():
                 "traffic": traffic_for(args.workload + (f"_n{n}" if n != 1 else "")),
                 "algorithmic_bytes_per_launch": alg // calls,
                 "us_per_launch": round(ms / calls * 1e3, 4),
+                "us_per_launch_isolated": iso,
                 "attainable_GB/s": att["GB/s"], "attainable_us": att["us"],
                 "frac_attainable": att["GB/s"] and round(achieved / att["GB/s"], 4),
                 "launch_floor_us": floor}

@@ -9,12 +9,13 @@
 // four VALU slots free; the weight decode costs 14 VALU operations per 8
 // weights, so every decoded B fragment is reused by four MFMAs.
 //
-// Tile: a workgroup of four waves computes 128 activation rows x 128 weight
-// rows.  Wave (wn, wk) owns weight rows [64 wn, 64 wn + 64) of the tile and
-// blocks 2 wk, 2 wk + 1 of every 4-block group (128 k) of the workgroup's K
-// slice: 4 x 2 accumulators of 32 x 32 against all 128 activation rows, so
-// each A fragment read from LDS feeds two MFMAs.  At the end the two K halves
-// are summed through LDS.
+// Tile: a workgroup computes 128 activation rows x 128 weight rows.  Wave
+// (wm, wn, wk) owns weight rows [64 wn, 64 wn + 64) of the tile, blocks
+// 2 wk, 2 wk + 1 of every 4-block group (128 k) of the workgroup's K slice
+// and, with eight waves, activation rows [64 wm, 64 wm + 64) (with four
+// waves all 128): 2 (or 4) x 2 accumulators of 32 x 32, so each A fragment
+// read from LDS feeds two MFMAs.  At the end the two K halves are summed
+// through LDS.
 //
 // Operands of one MFMA (K = 16, half a Q4_0 block):
 //   A: lane l = 32h + m holds activation row m of its 32-row sub-tile at
@@ -48,17 +49,30 @@ namespace q4 {
 
 constexpr int kGemmBM = 128;                 // activation rows per workgroup
 constexpr int kGemmBN = 128;                 // weight rows per workgroup
-constexpr int kGemmWaves = 4;
-constexpr int kGemmMSub = kGemmBM / 32;      // 32-row sub-tiles per wave
+// Waves per workgroup: 4 (one per SIMD, each wave 128 activation rows x 64
+// weight rows x half of K) or 8 (two per SIMD, each wave 64 x 64 x half of
+// K: the two activation halves decode the same weights, and while one wave
+// of a SIMD waits or decodes, the other's products keep the matrix unit
+// busy).
+#ifndef Q4_GEMM_WAVES
+#define Q4_GEMM_WAVES 4
+#endif
+constexpr int kGemmWaves = Q4_GEMM_WAVES;
+static_assert(kGemmWaves == 4 || kGemmWaves == 8, "4 or 8 waves");
+constexpr int kThreads = kGemmWaves * 64;
+constexpr int kGemmMHalves = kGemmWaves / 4;           // waves along the activation rows
+constexpr int kGemmMSub = kGemmBM / 32 / kGemmMHalves;  // 32-row sub-tiles per wave
 constexpr int kStepBytes = kGemmBM * 128 * 2;  // one step's x tile: 32 KB
-constexpr int kPiecesPerThread = kStepBytes / 16 / (kGemmWaves * 64);  // 8
+constexpr int kPiecesPerThread = kStepBytes / 16 / kThreads;  // 8 or 4
+constexpr int kPiecesPerPart = (kPiecesPerThread + 2) / 3;    // x pieces in parts 0..2
+constexpr int kTilesPerWave = 8 / kGemmWaves;     // 16-row code tiles a wave copies
 constexpr int kXBytes = kStepBytes;              // x part of a stage
 constexpr int kWBytes = 8 * kGroupCodeBytes;      // code words of the 8 repacked tiles
-constexpr int kSBytes = 4 * 1024;                 // their scales: a 1 KB slot per wave
-constexpr int kStageBytes = kXBytes + kWBytes + kSBytes;   // 44 KB
-constexpr int kStages = 3;                        // LDS ring: 132 KB
-constexpr int kCopies = kPiecesPerThread + 3;     // copies per wave per step (binary16 x)
-constexpr int kCopyParts012 = 9;                  // copies in parts 0..2 of a step
+constexpr int kSBytes = kGemmWaves * 1024;        // their scales: a 1 KB slot per wave
+constexpr int kStageBytes = kXBytes + kWBytes + kSBytes;   // 44 or 48 KB
+constexpr int kStages = 3;                        // LDS ring: 132 or 144 KB
+constexpr int kCopies = kPiecesPerThread + kTilesPerWave + 1;  // copies per wave per step
+constexpr int kCopyParts012 = kPiecesPerThread + 1;   // of them in parts 0..2 of a step
 constexpr int kTileStride = 136;                  // epilogue tile row, floats
 constexpr int kEpiBytes = kGemmBM * kTileStride * 4;   // 68 KB
 constexpr int kGemmLds = kStages * kStageBytes > kEpiBytes ? kStages * kStageBytes : kEpiBytes;
@@ -104,7 +118,7 @@ __device__ __forceinline__ u4_t to_half8(const X8 &v) {
 
 
 template <typename XT>
-__global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // kGemmLds bytes
     constexpr bool kDma = sizeof(XT) == 2;
     const int tid = threadIdx.x;
@@ -136,7 +150,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     }
     const int mb = tile % a.nm;
     const int nb = tile / a.nm;
-    const int wn = wave & 1, wk = wave >> 1;
+    const int wn = wave & 1, wk = (wave >> 1) & 1, wm = wave >> 2;
     const int m0 = mb * kGemmBM;
     const int nsteps = gs1 - gs0;
     const XT *__restrict__ x = (const XT *)a.x;
@@ -147,64 +161,67 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     // row r sits in slot r * 16 + (q ^ (r & 15)).  A copy instruction fills 64
     // consecutive slots = 4 whole rows (coalesced reads); the fragment reads
     // hit 16 distinct slot columns per 16 lanes (no bank conflict).  Wave w
-    // fills rows 32 w .. 32 w + 31, copy i rows 32 w + 4 i + lane / 16.  Rows
+    // fills rows R w .. R w + R - 1 (R = 4 x pieces per thread), copy i rows
+    // R w + 4 i + lane / 16.  Rows
     // past n repeat row n - 1 (a D row depends only on its own A row, and
     // those rows are not stored); in a group that runs past in, k >= in is
     // zero.
     // W: the group's code words of the tile's 8 repacked 16-row tiles (1 KB
-    // each, as stored) and their scales; wave w copies tiles 2w, 2w + 1 and
-    // their scales (lanes 0..15 carry the 256 scale bytes, the other lanes
-    // repeat them into the rest of the wave's 1 KB scale slot, so the copy
-    // needs no branch).  Tiles past the matrix read the last tile (their
-    // scales are forced to zero when used).
+    // each, as stored) and their scales; wave w copies T = 8 / waves tiles
+    // Tw .. Tw + T - 1 and their scales (lanes 0..8T-1 carry the 128 T scale
+    // bytes, the other lanes repeat them into the rest of the wave's 1 KB
+    // scale slot, so the copy needs no branch).  Tiles past the matrix read
+    // the last tile (their scales are forced to zero when used).
     uint32_t xoff[kPiecesPerThread];
 #pragma unroll
     for (int i = 0; i < kPiecesPerThread; ++i) {
-        const int r = 32 * wave + 4 * i + (lane >> 4);
+        const int r = 4 * kPiecesPerThread * wave + 4 * i + (lane >> 4);
         const int q = (lane & 15) ^ (r & 15);
         const int rr = m0 + r < a.n ? r : a.n - 1 - m0;
         xoff[i] = ((uint32_t)rr * a.in + 8 * q) * (uint32_t)sizeof(XT);
     }
     const XT *xbase = x + (int64_t)m0 * a.in;
     const int t0 = nb * (kGemmBN / kTileRows);               // first repacked tile
-    int tw[2];
+    int tw[kTilesPerWave];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int t = t0 + 2 * wave + u;
+    for (int u = 0; u < kTilesPerWave; ++u) {
+        const int t = t0 + kTilesPerWave * wave + u;
         tw[u] = t < a.tiles ? t : a.tiles - 1;
     }
-    const int ts = tw[(lane >> 3) & 1];
+    const int ts = tw[((lane >> 3) & 1) % kTilesPerWave];
     const uint32_t soff_copy = (uint32_t)ts * a.g4 * kGroupScaleBytes + (lane & 7) * 16;
 
-    // part p of step st's copies: x pieces 3p .. 3p+2 (binary16 x only),
-    // code tile 2w at p = 2, code tile 2w + 1 and the scales at p = 3
+    // part p < 3 of step st's copies: x pieces P p .. P p + P - 1 (binary16
+    // x only, P = kPiecesPerPart); code tile u of the wave at part 2 + u; the
+    // scales at part 3
     auto fill = [&](int st, int part, bool partial) {
         const int j = gs0 + st;
         uint8_t *stage = lds + (st % kStages) * kStageBytes;
         if constexpr (kDma) {
-            uint8_t *xd = stage + wave * 8192;
+            uint8_t *xd = stage + wave * (kPiecesPerThread * 1024);
             const uint8_t *src = (const uint8_t *)(xbase + j * 128);
 #pragma unroll
             for (int i = 0; i < kPiecesPerThread; ++i) {
-                if (i < 3 * part || i >= (part < 2 ? 3 * part + 3 : kPiecesPerThread)) continue;
+                if (part > 2 || i < kPiecesPerPart * part || i >= kPiecesPerPart * (part + 1))
+                    continue;
                 const void *p = src + xoff[i];
                 if (partial) {
-                    const int r = 32 * wave + 4 * i + (lane >> 4);
+                    const int r = 4 * kPiecesPerThread * wave + 4 * i + (lane >> 4);
                     const int q = (lane & 15) ^ (r & 15);
                     p = j * 128 + 8 * q < a.in ? p : (const void *)&kZeroPiece;
                 }
                 dma16(p, xd + i * 1024);
             }
         }
-        if (part == 2)
-            dma16(a.packed + a.code_base + ((int64_t)tw[0] * a.g4 + j) * kGroupCodeBytes + lane * 16,
-                  stage + kXBytes + (2 * wave) * 1024);
-        if (part == 3) {
-            dma16(a.packed + a.code_base + ((int64_t)tw[1] * a.g4 + j) * kGroupCodeBytes + lane * 16,
-                  stage + kXBytes + (2 * wave + 1) * 1024);
+#pragma unroll
+        for (int u = 0; u < kTilesPerWave; ++u)
+            if (part == 2 + u)
+                dma16(a.packed + a.code_base + ((int64_t)tw[u] * a.g4 + j) * kGroupCodeBytes +
+                          lane * 16,
+                      stage + kXBytes + (kTilesPerWave * wave + u) * 1024);
+        if (part == 3)
             dma16(a.packed + (int64_t)j * kGroupScaleBytes + soff_copy,
                   stage + kXBytes + kWBytes + wave * 1024);
-        }
     };
     X8 xp[kDma ? 1 : kPiecesPerThread];
     auto fetch = [&](int st) {                     // register path (float32 x): load
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
             const uint8_t *src = (const uint8_t *)(xbase + j * 128);
 #pragma unroll
             for (int i = 0; i < kPiecesPerThread; ++i) {
-                const int r = 32 * wave + 4 * i + (lane >> 4);
+                const int r = 4 * kPiecesPerThread * wave + 4 * i + (lane >> 4);
                 const int q = (lane & 15) ^ (r & 15);
                 const bool ok = j * 128 + 8 * q < a.in;
                 xp[i] = load_x8((const float *)(src + xoff[i]), ok);
@@ -222,7 +239,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     };
     auto park = [&](int st) {                      // register path: convert, write the stage
         if constexpr (!kDma) {
-            uint8_t *xd = lds + (st % kStages) * kStageBytes + wave * 8192 + lane * 16;
+            uint8_t *xd = lds + (st % kStages) * kStageBytes + wave * (kPiecesPerThread * 1024) +
+                          lane * 16;
 #pragma unroll
             for (int i = 0; i < kPiecesPerThread; ++i)
                 *reinterpret_cast<u4_t *>(xd + i * 1024) = to_half8(xp[i]);
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     // weight words of the lane in a stage: sub-tile ni = rows 64 wn + 32 ni + c
     // = tile 4 wn + 2 ni + c / 16, row c % 16; quarter 2h (+1: 256 bytes on),
     // blocks 2 wk, 2 wk + 1 (8 bytes); their scales (4 bytes) in the slot of
-    // the wave that copied the tile
+    // the wave that copied the tile (128 bytes per tile in the slot)
     uint32_t woff[2], sgoff[2];
     bool wvalid[2];
 #pragma unroll
@@ -243,7 +261,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
         const int tl = 4 * wn + 2 * ni + (c >> 4);
         wvalid[ni] = t0 + tl < a.tiles;
         woff[ni] = kXBytes + tl * 1024 + ((2 * h) * 16 + (c & 15)) * 16 + 8 * wk;
-        sgoff[ni] = kXBytes + kWBytes + (tl >> 1) * 1024 + (tl & 1) * 128 + (c & 15) * 8 + 4 * wk;
+        sgoff[ni] = kXBytes + kWBytes + (tl / kTilesPerWave) * 1024 + (tl % kTilesPerWave) * 128 +
+                    (c & 15) * 8 + 4 * wk;
     }
 
     f16x_t acc[kGemmMSub][2];
@@ -304,7 +323,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
 #pragma unroll
         for (int mi = 0; mi < kGemmMSub; ++mi)
             av[mi] = __builtin_bit_cast(
-                h8_t, *reinterpret_cast<const u4_t *>(stage + aoff[4 * wk + kq] + mi * 8192));
+                h8_t, *reinterpret_cast<const u4_t *>(stage + aoff[4 * wk + kq] +
+                                                     (kGemmMSub * wm + mi) * 8192));
     };
     // operands of K-step 0 of step st into buffer 0
     auto prep_first = [&](int st) {
@@ -319,12 +339,13 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     // matrix pipe takes it, so only work placed between the products
     // overlaps them; the scheduling groups enforce that order inside the
     // (branch-free) region.
+    constexpr int kValuPerMfma = 16 / kGemmMSub;                 // 4 or 8
     auto interleave = [&]() {
 #pragma unroll
         for (int i = 0; i < 2 * kGemmMSub; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -377,13 +398,14 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
             // next step's weight words first, two products while they
             // travel, then the decode between the remaining products
             prep_first(st + 1);
+            constexpr int kLead = kGemmMSub / 2;                    // products while words travel
             __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);      // DS read: words, scales
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);  // MFMA
 #pragma unroll
-            for (int i = 0; i < 6; ++i) {
+            for (int i = 0; i < 2 * kGemmMSub - kLead; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: A
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * kGemmMSub - kLead), 0);  // VALU
             }
             __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -440,7 +462,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     // lane holds tile column 64 wn + 32 ni + c, tile rows
     // 32 mi + 8 (v / 4) + 4 h + v % 4
     auto tix = [&](int mi, int ni, int v) {
-        return (32 * mi + 8 * (v >> 2) + 4 * h + (v & 3)) * kTileStride + 64 * wn + 32 * ni + c;
+        return (32 * (kGemmMSub * wm + mi) + 8 * (v >> 2) + 4 * h + (v & 3)) * kTileStride +
+               64 * wn + 32 * ni + c;
     };
     if (wk == 1) {
 #pragma unroll
@@ -474,8 +497,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
         // a K slice: the whole 128 x 128 partial tile, row-major, to the workspace
         float *dst = a.part + (int64_t)piece * kGemmBM * kGemmBN;
 #pragma unroll 4
-        for (int it = 0; it < kGemmBM * kGemmBN / 4 / (kGemmWaves * 64); ++it) {
-            const int e = it * kGemmWaves * 64 + tid;          // float4 index in the tile
+        for (int it = 0; it < kGemmBM * kGemmBN / 4 / kThreads; ++it) {
+            const int e = it * kThreads + tid;                 // float4 index in the tile
             const int row = e >> 5, col = (e & 31) * 4;
             __builtin_nontemporal_store(*reinterpret_cast<const f4_t *>(ttile + row * kTileStride + col),
                                         reinterpret_cast<f4_t *>(dst + row * kGemmBN + col));
@@ -484,8 +507,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_kernel(const GemmArgs
     }
     const bool full_cols = n0 + kGemmBN <= a.out && (a.out & 3) == 0;
 #pragma unroll 4
-    for (int it = 0; it < kGemmBM * kGemmBN / 4 / (kGemmWaves * 64); ++it) {
-        const int e = it * kGemmWaves * 64 + tid;              // float4 index in the tile
+    for (int it = 0; it < kGemmBM * kGemmBN / 4 / kThreads; ++it) {
+        const int e = it * kThreads + tid;                     // float4 index in the tile
         const int row = e >> 5, col = (e & 31) * 4;
         if (m0 + row >= a.n) continue;
         const float4 v = *reinterpret_cast<const float4 *>(ttile + row * kTileStride + col);
@@ -619,7 +642,7 @@ hipError_t launch_gemm(const void *packed, const void *x, int x_f16, float *y, i
     a.dies = device_shape().dies;
     a.die_full = (p.full > 0 && p.full % a.dies == 0) ? 1 : 0;
     a.die_split = (p.rem > 0 && (p.rem * p.split) % a.dies == 0) ? 1 : 0;
-    const dim3 grid((unsigned)p.wgs), block(kGemmWaves * 64);
+    const dim3 grid((unsigned)p.wgs), block(kThreads);
     const size_t lds = (size_t)kGemmLds;
     if (x_f16)
         hipLaunchKernelGGL(gemm_kernel<_Float16>, grid, block, lds, stream, a);

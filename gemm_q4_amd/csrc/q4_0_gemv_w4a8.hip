@@ -40,14 +40,15 @@ namespace {
 constexpr int kW8MaxWaves = 8;
 constexpr int kW8MaxRows = 16;
 constexpr int kW8Groups = 5;          // groups a wave holds (A: 8 registers each)
-// Workgroups a launch aims for: about four per compute unit from
-// kW8ManyTiles tile-slices on, about one below (each workgroup walks a run
-// of tiles with its activation codes, as in the binary16 small-n kernel).
-#ifndef Q4_W8_TARGET_WGS_SMALL
-#define Q4_W8_TARGET_WGS_SMALL 256
+// Workgroups a launch aims for, per compute unit of the device: this many
+// from kW8ManyTiles tile-slices on, one below (each workgroup walks a run of
+// tiles with its activation codes, as in the binary16 small-n kernel).
+#ifndef Q4_W8_WGS_PER_CU
+#define Q4_W8_WGS_PER_CU 4
 #endif
-constexpr int kW8TargetWgs = 1024;
-constexpr int kW8TargetWgsSmall = Q4_W8_TARGET_WGS_SMALL;
+#ifndef Q4_W8_WGS_PER_CU_SMALL
+#define Q4_W8_WGS_PER_CU_SMALL 1
+#endif
 constexpr int64_t kW8ManyTiles = 4096;
 constexpr int kW8ReduceBatch = 8;     // slice loads in flight per thread
 constexpr int kW8RedTiles = 2;
@@ -294,7 +295,9 @@ W8Plan w8_plan(int64_t out, int64_t in) {
     p.per = (int)((p.gps + waves - 1) / waves);
     p.waves = (int)((p.gps + p.per - 1) / p.per);
     const int64_t units = L.tiles * p.slices;
-    const int64_t target = units >= kW8ManyTiles ? kW8TargetWgs : kW8TargetWgsSmall;
+    const int64_t cus = device_shape().cus;
+    const int64_t target =
+        cus * (units >= kW8ManyTiles ? Q4_W8_WGS_PER_CU : Q4_W8_WGS_PER_CU_SMALL);
     int64_t tpw = (units + target - 1) / target;
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
