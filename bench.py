@@ -107,9 +107,13 @@ def ws_tensor(torch, nbytes):
 
 
 class Case:
-    """One linear: repacked copies of W, an x, a y and a workspace on the device."""
+    """One linear: repacked copies of W, copies of x (the same values: step i
+    reads x copy i % copies, so x comes from memory, as an activation just
+    written by the previous kernel would, not from a cache warmed by the
+    step before; warm_x keeps one copy), a y and a workspace on the device."""
 
-    def __init__(self, torch, q4, synth, out, in_, n, x_dtype, seed, copies, kernel=0):
+    def __init__(self, torch, q4, synth, out, in_, n, x_dtype, seed, copies, kernel=0,
+                 warm_x=False):
         self.out, self.in_, self.n = out, in_, n
         blk = synth.make_blocks(out, in_, seed=seed)
         b = torch.from_numpy(blk.reshape(-1)).cuda()
@@ -117,7 +121,9 @@ class Case:
         del b
         self.packed = [base] + [base.clone() for _ in range(copies - 1)]
         npdt = np.float16 if x_dtype == "f16" else np.float32
-        self.x = torch.from_numpy(synth.make_x(n, in_, seed=seed + 1000, dtype=npdt)).cuda()
+        x0 = torch.from_numpy(synth.make_x(n, in_, seed=seed + 1000, dtype=npdt)).cuda()
+        self.xs = [x0] + [x0.clone() for _ in range(0 if warm_x else copies - 1)]
+        self.x = x0
         self.xcode = q4.F16 if x_dtype == "f16" else q4.F32
         self.y = torch.empty((n, out), dtype=torch.float32, device="cuda")
         self.wbytes = q4.q4_0_blocks_bytes(out, in_)
@@ -226,24 +232,25 @@ def timed(torch, q4, cases, steps, warmup, graph=True, groups=None, argmax=False
     def step(i, sh):
         if w4a8:
             for c in cases:
-                q4.q4_0_quantize_x8(c.x, c.xcode, c.q8, c.d8, c.n, c.in_, sh)
+                q4.q4_0_quantize_x8(c.xs[i % len(c.xs)], c.xcode, c.q8, c.d8, c.n, c.in_, sh)
                 q4.q4_0_matmul_w4a8(c.packed[i % ncopy], c.q8, c.d8, c.y, c.n, c.out, c.in_,
                                     c.wws, c.wneed, sh)
             return
         if argmax:
             for c in cases:
-                q4.q4_0_matmul_argmax(c.packed[i % ncopy], c.x, c.xcode, None, c.n, c.out,
-                                      c.in_, c.mv, c.mi, c.aws, c.aneed, sh)
+                q4.q4_0_matmul_argmax(c.packed[i % ncopy], c.xs[i % len(c.xs)], c.xcode, None,
+                                      c.n, c.out, c.in_, c.mv, c.mi, c.aws, c.aneed, sh)
             return
         if groups is None:
             for c in cases:
-                q4.q4_0_matmul_ex(c.packed[i % ncopy], c.x, c.xcode, c.y, c.n, c.out,
-                                  c.in_, c.kernel, c.ws, c.ws_need, sh)
+                q4.q4_0_matmul_ex(c.packed[i % ncopy], c.xs[i % len(c.xs)], c.xcode, c.y, c.n,
+                                  c.out, c.in_, c.kernel, c.ws, c.ws_need, sh)
             return
         for grp, (ws, need) in zip(groups, gws):
             q4.q4_0_matmul_grouped(
-                [(cases[k].packed[i % ncopy], cases[k].x, cases[k].y, cases[k].out,
-                  cases[k].in_) for k in grp], cases[grp[0]].xcode, cases[grp[0]].n, ws, need,
+                [(cases[k].packed[i % ncopy], cases[k].xs[i % len(cases[k].xs)], cases[k].y,
+                  cases[k].out, cases[k].in_) for k in grp], cases[grp[0]].xcode,
+                cases[grp[0]].n, ws, need,
                 sh)
 
     return time_steps(torch, step, steps, warmup, graph)
@@ -261,6 +268,7 @@ class Calibration:
     replay, the best of several grid sizes)."""
 
     GRIDS = (256, 512, 1024, 2048, 4096)
+    FLOOR_GRID = 250      # the empty launch's grid: told apart from the reads in a trace
 
     def __init__(self, torch, q4):
         self.torch, self.q4 = torch, q4
@@ -290,11 +298,12 @@ class Calibration:
     def launch_floor_us(self, steps=500):
         if self.floor is None:
             q4, sink = self.q4, self.sink
-            ms = time_steps(self.torch, lambda i, sh: q4.q4_0_stream_read(None, 0, sink, 256, sh),
+            g = self.FLOOR_GRID
+            ms = time_steps(self.torch, lambda i, sh: q4.q4_0_stream_read(None, 0, sink, g, sh),
                             steps, 20)
             self.floor = round(ms * 1e3, 3)
             self.floor_isolated = self.isolated_us(
-                lambda i, sh: q4.q4_0_stream_read(None, 0, sink, 256, sh))
+                lambda i, sh: q4.q4_0_stream_read(None, 0, sink, g, sh))
         return self.floor
 
     def read(self, nbytes, steps=200):
@@ -592,8 +601,16 @@ def main():
             c = cases[0]
             ncp = len(c.packed)
             iso = cal.isolated_us(lambda i, sh: q4.q4_0_matmul_ex(
-                c.packed[i % ncp], c.x, c.xcode, c.y, c.n, c.out, c.in_, c.kernel, c.ws,
-                c.ws_need, sh))
+                c.packed[i % ncp], c.xs[i % len(c.xs)], c.xcode, c.y, c.n, c.out, c.in_,
+                c.kernel, c.ws, c.ws_need, sh))
+        # the same steps with one x for every step (x warm in the caches)
+        xs_saved = [c.xs for c in cases]
+        for c in cases:
+            c.xs = c.xs[:1]
+        ms_warm_x = timed(torch, q4, cases, args.steps, args.warmup, groups=groups,
+                          argmax=args.argmax, w4a8=args.w4a8)
+        for c, xs in zip(cases, xs_saved):
+            c.xs = xs
         parity = None if (args.argmax or args.w4a8) else max(
             parity_check(q4, __import__("oracle"), synth, c, seed=k) for k, c in enumerate(cases))
         value = total_w / (ms * 1e-3) / 1e9
@@ -621,6 +638,8 @@ def main():
                "timing": "HIP graph replay of the step's launches, events on the launch stream",
                "grouped": groups is not None, "argmax": args.argmax, "w4a8": args.w4a8,
                "ms_per_step_eager": round(ms_eager, 6),
+               "ms_per_step_warm_x": round(ms_warm_x, 6),
+               "x_copies": len(cases[0].xs),
                # the products: binary16 operands (x as high and low parts up to
                # 8 rows), float32 accumulation; W4A8: int8 operands, int32 sums
                "accumulate": "i32 then f32" if args.w4a8 else "f32"}

@@ -58,6 +58,11 @@ constexpr int kGemmBN = 128;                 // weight rows per workgroup
 #define Q4_GEMM_WAVES 4
 #endif
 constexpr int kGemmWaves = Q4_GEMM_WAVES;
+// Partial tiles of the K slices stored with non-temporal stores (1) or plain
+// stores (0: they stay in the caches for the reduction kernel that follows).
+#ifndef Q4_GEMM_NT_PARTIALS
+#define Q4_GEMM_NT_PARTIALS 1
+#endif
 static_assert(kGemmWaves == 4 || kGemmWaves == 8, "4 or 8 waves");
 constexpr int kThreads = kGemmWaves * 64;
 constexpr int kGemmMHalves = kGemmWaves / 4;           // waves along the activation rows
@@ -500,8 +505,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
         for (int it = 0; it < kGemmBM * kGemmBN / 4 / kThreads; ++it) {
             const int e = it * kThreads + tid;                 // float4 index in the tile
             const int row = e >> 5, col = (e & 31) * 4;
-            __builtin_nontemporal_store(*reinterpret_cast<const f4_t *>(ttile + row * kTileStride + col),
-                                        reinterpret_cast<f4_t *>(dst + row * kGemmBN + col));
+            const f4_t v = *reinterpret_cast<const f4_t *>(ttile + row * kTileStride + col);
+            f4_t *d = reinterpret_cast<f4_t *>(dst + row * kGemmBN + col);
+#if Q4_GEMM_NT_PARTIALS
+            __builtin_nontemporal_store(v, d);
+#else
+            *d = v;
+#endif
         }
         return;
     }

@@ -133,14 +133,16 @@ constexpr int kMaxStageItems = 10;
 // (xprep_kernel) instead of by every workgroup.  Measured on MI355X (graph
 // replay, workgroups walking runs of tiles): FFN-up 9728 x 2560 at n = 4/5/6
 // takes 8.0/8.9/14.6 us with per-workgroup conversion against 8.7/9.1/9.7 us
-// with the pre-pass; the 151936-row head at n = 4 takes 49 us against 46 us.
-// So the pre-pass from 6 rows, and from 4 rows for matrices of at least
+// with the pre-pass.  The 151936-row head at n = 4, two workgroups per
+// compute unit: 40.8 us converting per workgroup against 41.0 us with the
+// pre-pass, and 45.2 against 46.7 us with the fused greedy pick.  So the
+// pre-pass from 6 rows, and from 5 rows for matrices of at least
 // kMfmaManyTiles tiles.
 #ifndef Q4_MFMA_PREP_MIN_N
 #define Q4_MFMA_PREP_MIN_N 6
 #endif
 #ifndef Q4_MFMA_PREP_MIN_N_LARGE
-#define Q4_MFMA_PREP_MIN_N_LARGE 4
+#define Q4_MFMA_PREP_MIN_N_LARGE 5
 #endif
 constexpr int kPrepMinN = Q4_MFMA_PREP_MIN_N;
 constexpr int kPrepMinNLarge = Q4_MFMA_PREP_MIN_N_LARGE;

@@ -137,9 +137,10 @@ def test_grouped_ragged_shapes_shared_x_and_k_split(n):
 
 @pytest.mark.parametrize("n", [4, 5, 6, 40])
 def test_grouped_matrices_of_both_sizes(n):
-    """At 4 and 5 rows a matrix of 4096 tiles or more converts x by a pre-pass
-    and a small one does not, so such a group runs as separate launches; from
-    6 rows both use it and share one launch; at 40 rows the large matrices
+    """At 4 rows no matrix converts x by a pre-pass and the group shares one
+    launch; at 5 rows a matrix of 4096 tiles or more does and a small one does
+    not, so such a group runs as separate launches; from 6 rows both use it
+    and share one launch; at 40 rows the large matrices
     take 32-row launches and the small one a 40-row launch, so the group runs
     as separate launches again.  Every output as single calls and within the
     small-n bound of the oracle."""
