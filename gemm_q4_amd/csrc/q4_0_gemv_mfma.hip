@@ -131,15 +131,19 @@ constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per work
 constexpr int kMaxStageItems = 10;
 // Activation rows from which x is converted once per launch by a pre-pass
 // (xprep_kernel) instead of by every workgroup.  Measured on MI355X (graph
-// replay, workgroups walking runs of tiles): FFN-up 9728 x 2560 at n = 4/5/6
-// takes 8.0/8.9/14.6 us with per-workgroup conversion against 8.7/9.1/9.7 us
-// with the pre-pass.  The 151936-row head at n = 4, two workgroups per
-// compute unit: 40.8 us converting per workgroup against 41.0 us with the
-// pre-pass, and 45.2 against 46.7 us with the fused greedy pick.  So the
-// pre-pass from 6 rows, and from 5 rows for matrices of at least
-// kMfmaManyTiles tiles.
+// replay, workgroups walking runs of tiles): FFN-up 9728 x 2560 at n = 4/5
+// takes 8.0/8.9 us with per-workgroup conversion against 8.7/9.1 us with the
+// pre-pass, and at n = 6/8 10.5/10.8 us against 10.2/10.4 us.  The block of
+// seven linears in one grouped call (its workgroups shared out over the
+// group: long runs of tiles, so each workgroup converts once for many
+// tiles) at n = 6/8 takes 24.1/24.6 us converting per workgroup against
+// 25.2/26.7 us with the pre-pass.  The 151936-row head at n = 4, two
+// workgroups per compute unit: 40.8 us converting per workgroup against 41.0
+// us with the pre-pass, and 45.2 against 46.7 us with the fused greedy pick.
+// So the pre-pass from 9 rows (where one binary16 part per row starts), and
+// from 5 rows for matrices of at least kMfmaManyTiles tiles.
 #ifndef Q4_MFMA_PREP_MIN_N
-#define Q4_MFMA_PREP_MIN_N 6
+#define Q4_MFMA_PREP_MIN_N 9
 #endif
 #ifndef Q4_MFMA_PREP_MIN_N_LARGE
 #define Q4_MFMA_PREP_MIN_N_LARGE 5
@@ -987,9 +991,11 @@ static int64_t frag_bytes(int64_t n, int64_t in) {
 }
 
 // Whether a launch with n rows against an [out x in] matrix uses the pre-pass.
-static bool use_prep(int64_t n, int64_t out, int64_t in) {
+// A by-expert launch (gathered) always does: its pre-pass gathers each
+// chunk's x rows through the routing plan.
+static bool use_prep(int64_t n, int64_t out, int64_t in, bool gathered = false) {
     if (frag_bytes(n, in) > (int64_t)(kWorkspaceBytes / 4)) return false;
-    if (n >= kPrepMinN) return true;
+    if (gathered || n >= kPrepMinN) return true;
     return n >= kPrepMinNLarge && Layout(out, in).tiles >= kMfmaManyTiles;
 }
 
@@ -999,9 +1005,9 @@ static int gpw_for(int64_t per, int64_t n, bool prep) {
     return 0;
 }
 
-static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in) {
+static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in, bool gathered = false) {
     const Layout L(out, in);
-    const bool prep = use_prep(n, out, in);
+    const bool prep = use_prep(n, out, in, gathered);
     n = kernel_rows(n);
     MfmaPlan p;
     // groups a wave may hold: the x it stages must fit its registers, or, when
@@ -1069,10 +1075,10 @@ static size_t launch_argmax_workspace_bytes(int64_t n, int64_t out, int64_t in) 
            (size_t)round256(amax_pairs(p, n, out, in) * (int64_t)sizeof(uint2));
 }
 
-static bool launch_supported(int64_t n, int64_t out, int64_t in) {
+static bool launch_supported(int64_t n, int64_t out, int64_t in, bool gathered = false) {
     if (n < 1 || n > kMaxRows) return false;
-    if (n > 16 && !use_prep(n, out, in)) return false;   // two A groups need prepared x
-    const MfmaPlan p = mfma_plan(n, out, in);
+    if (n > 16 && !use_prep(n, out, in, gathered)) return false;  // two A groups: prepared x
+    const MfmaPlan p = mfma_plan(n, out, in, gathered);
     if (p.gpw == 0 || p.waves > kMfmaMaxWaves || p.slices > 65535) return false;
     if ((int64_t)p.waves * p.per < p.gps) return false;
     if (p.gx * p.slices > 0x7fffffff) return false;
@@ -1198,11 +1204,12 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
     ra.nrows = (int)nrows;
     int waves = 1, gpw = 0;
     int64_t wg = 0, wsoff = 0;
-    bool prep = true;
-    // the linears of a group agree on the pre-pass (gemv_mfma_group_uniform)
-    for (int i = 0; i < count; ++i) prep = prep && use_prep(nrows, probs[i].out, probs[i].in);
     // by column: one unprepared row per pair; by expert: prepared chunks of kChunkRows rows
     const bool by_expert = route && route->chunk_expert;
+    bool prep = true;
+    // the linears of a group agree on the pre-pass (gemv_mfma_group_uniform)
+    for (int i = 0; i < count; ++i)
+        prep = prep && use_prep(nrows, probs[i].out, probs[i].in, by_expert);
     if (route && (by_expert ? (!prep || nrows != kChunkRows || NT != kChunkRows) : prep))
         return hipErrorInvalidValue;
     // a group: the weight groups of all its linears, for the shared target
@@ -1214,7 +1221,7 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         }
     for (int i = 0; i < count; ++i) {
         const GemvProblem &pr = probs[i];
-        MfmaPlan p = mfma_plan(nrows, pr.out, pr.in);
+        MfmaPlan p = mfma_plan(nrows, pr.out, pr.in, by_expert);
         const Layout L(pr.out, pr.in);
         if (count > 1) {
             // this linear's share of the group's workgroups (the runs of
@@ -1476,7 +1483,7 @@ static int64_t by_expert_table_bytes(int64_t chunks) {
 size_t gemv_mfma_by_expert_workspace_bytes(int64_t n, int64_t k, int64_t n_experts, int64_t out,
                                            int64_t in) {
     const int64_t c = max_chunks(n * k, n_experts);
-    const MfmaPlan p = mfma_plan(kChunkRows, out, in);
+    const MfmaPlan p = mfma_plan(kChunkRows, out, in, true);
     return (size_t)(by_expert_table_bytes(c) + c * (int64_t)mfma_part_bytes(p, out, in) +
                     (n + kChunkRows - 1) / kChunkRows * frag_bytes(kChunkRows, in));
 }
@@ -1486,8 +1493,9 @@ bool gemv_mfma_by_expert_supports(int64_t n, int64_t k, int64_t n_experts, int64
     const int64_t pairs = n * k;
     if (pairs < 1 || pairs > kPlanMaxPairs || n_experts < 1 || n_experts + 1 > kPlanMaxBuckets)
         return false;
-    if (!launch_supported(kChunkRows, out, in) || !use_prep(kChunkRows, out, in)) return false;
-    const MfmaPlan p = mfma_plan(kChunkRows, out, in);
+    if (!launch_supported(kChunkRows, out, in, true) || !use_prep(kChunkRows, out, in, true))
+        return false;
+    const MfmaPlan p = mfma_plan(kChunkRows, out, in, true);
     return p.gx * p.slices * max_chunks(pairs, n_experts) <= 0x7fffffff &&
            gemv_mfma_by_expert_workspace_bytes(n, k, n_experts, out, in) <= kWorkspaceBytes;
 }

@@ -135,12 +135,12 @@ def test_grouped_ragged_shapes_shared_x_and_k_split(n):
         assert ratio(yy, blk, x, out, in_) <= TOL_SMALL_N
 
 
-@pytest.mark.parametrize("n", [4, 5, 6, 40])
+@pytest.mark.parametrize("n", [4, 5, 6, 12, 40])
 def test_grouped_matrices_of_both_sizes(n):
     """At 4 rows no matrix converts x by a pre-pass and the group shares one
-    launch; at 5 rows a matrix of 4096 tiles or more does and a small one does
-    not, so such a group runs as separate launches; from 6 rows both use it
-    and share one launch; at 40 rows the large matrices
+    launch; at 5 and 6 rows a matrix of 4096 tiles or more does and a small
+    one does not, so such a group runs as separate launches; from 9 rows both
+    use it and share one launch (checked at 12); at 40 rows the large matrices
     take 32-row launches and the small one a 40-row launch, so the group runs
     as separate launches again.  Every output as single calls and within the
     small-n bound of the oracle."""
@@ -674,13 +674,15 @@ def test_routed_moe_full_size():
 
 # ------------------------------------------------------------------ routed (by expert)
 @pytest.mark.parametrize("n,k,out,in_", [(3, 2, 300, 160), (20, 4, 37, 4128),
-                                         (9, 3, 64, 9728)])
+                                         (9, 3, 64, 9728), (5, 2, 65536, 128)])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16], ids=["xf32", "xf16"])
-def test_routed_by_expert_equals_8_row_calls_and_oracle(n, k, out, in_, xdt):
-    """By expert, each pair's row equals row 0 of the 8-row product of its
-    expert with its x row (the chunk's instance) bit for bit, whichever chunk
-    and row the plan gave it, and matches the oracle.  Six experts for up to
-    80 pairs: buckets of several chunks, partial last chunks."""
+def test_routed_by_expert_rows_do_not_depend_on_the_plan(n, k, out, in_, xdt):
+    """By expert, each pair's row equals the by-expert product of that pair
+    alone bit for bit, whichever chunk and row the plan gave it, and matches
+    the oracle.  Six experts for up to 80 pairs: buckets of several chunks,
+    partial last chunks.  For the matrix of 4096 tiles, where an ordinary
+    8-row call prepares x as well, the row also equals row 0 of the 8-row
+    product of its expert with its x row (the chunk's instance)."""
     n_exp = 6
     blks, stack = _expert_stack(n_exp, out, in_, seed=100)
     x = synth.make_x(n, in_, seed=101, dtype=xdt)
@@ -694,11 +696,16 @@ def test_routed_by_expert_equals_8_row_calls_and_oracle(n, k, out, in_, xdt):
     assert np.array_equal(yy, y2.cpu().numpy())          # the plan's order does not matter
     pb = q4.q4_0_packed_bytes(out, in_)
     for t in range(n):
-        x8 = np.repeat(x[t:t + 1], 8, axis=0)
         for j in range(k):
             p, e = t * k + j, int(route[t, j])
-            single = run(stack[e * pb:(e + 1) * pb], x8, out, kernel=q4.KERNEL_GEMV_MFMA)
-            assert np.array_equal(yy[p], single[0]), (t, j, e)
+            alone = q4.matmul_routed(stack, n_exp, to_dev(x[t:t + 1]),
+                                     to_dev(np.array([[e]], dtype=np.int32)), out,
+                                     route_kernel=q4.ROUTE_BY_EXPERT).cpu().numpy()
+            assert np.array_equal(yy[p], alone[0]), (t, j, e)
+            if out >= 65536:
+                x8 = np.repeat(x[t:t + 1], 8, axis=0)
+                single = run(stack[e * pb:(e + 1) * pb], x8, out, kernel=q4.KERNEL_GEMV_MFMA)
+                assert np.array_equal(yy[p], single[0]), (t, j, e)
             assert ratio(yy[p:p + 1], blks[e], x[t:t + 1], out, in_) <= TOL_SMALL_N
 
 
