@@ -504,7 +504,7 @@ __global__ __launch_bounds__(kPrepThreads) void route_prep_kernel(
 // wave's range, slot j and quarter g as in xprep_kernel, 16 bytes at
 // ((bl * 2*NT + j) * 4 + g) * 16 of the wave's LDS region.  A prepared launch
 // loads each lane's own fragments of its range straight into registers.
-template <int NT, typename XT, int GPW, bool PREP>
+template <int NT, typename XT, int GPW, bool PREP, bool IDLE>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const GemvArgs args) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int kRedTiles = red_tiles<NT>();
@@ -553,6 +553,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // this wave's groups of the slice: [q0, q0 + ng)
     const int q0 = wave * a.per;
     const int ng = gsn - q0 < 0 ? 0 : (gsn - q0 < a.per ? gsn - q0 : a.per);
+    // IDLE instance (a group of linears whose launch has more waves than some
+    // linear's plan): waves without groups walk the tiles without requests
+    // or products and only join the reductions, whose sums stop at the last
+    // wave with groups (the terms left out are exact zeros).  Other launches
+    // keep the branch-free loop.
+    const int nact = IDLE ? (gsn + a.per - 1) / a.per : nwaves;
+    const bool idle = IDLE && ng == 0;
     const int tb = cx * a.tpw;                                // < tiles by the plan
     const int te = tb + a.tpw < a.tiles ? tb + a.tpw : a.tiles;
     const XT *__restrict__ x = (const XT *)a.x;
@@ -829,7 +836,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             const int tt = (e >> 4) % NT, rr = e & 15;
             const int t = t0 + sl;
             float sum = 0.0f;
-            for (int w = 0; w < nwaves; ++w) sum += red[sl][w][tt][rr];
+            for (int w = 0; w < nact; ++w) sum += red[sl][w][tt][rr];
             if (!split) {
                 const int row = t * kTileRows + rr;
                 if (row < a.out && tt < args.nrows) {
@@ -856,13 +863,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     // stored inside the loop only when a run exceeds kRedTiles tiles.
     int t0 = tb, t = tb;
     for (; t + 1 < te; ++t) {
-        tile(t, t - t0, true);
+        if (!idle) tile(t, t - t0, true);
         if (t - t0 == kRedTiles - 1) {
             flush(t0, kRedTiles);
             t0 = t + 1;
         }
     }
-    tile(t, t - t0, false);
+    if (!idle) tile(t, t - t0, false);
     flush(t0, t - t0 + 1);
     if constexpr (NT <= kArgmaxRows)
         if (a.amax && !split) amax_workgroup<NT>(bv, bi, a.amax + (int64_t)local * NT);
@@ -1161,28 +1168,43 @@ bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n) {
 
 // Launches the instance if it exists (its groups fit the registers); returns
 // whether it did.
+// (idle: some linear of the launch plans fewer waves than the launch has; only
+// unprepared launches have an IDLE instance, measured below)
 template <int NT, typename XT, int GPW, bool PREP>
-static bool launch_mfma_g(dim3 gd, dim3 bd, size_t lds, hipStream_t stream, const GemvArgs &a) {
+static bool launch_mfma_g(bool idle, dim3 gd, dim3 bd, size_t lds, hipStream_t stream,
+                          const GemvArgs &a) {
     if constexpr (PREP ? GPW <= prep_max_groups<NT>()
                        : (NT <= 16 && ((int64_t)GPW * 16 * NT + 63) / 64 <= kMaxStageItems)) {
-        hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW, PREP>), gd, bd, lds, stream, a);
+        if constexpr (!PREP && NT <= 8)
+            if (idle) {
+                hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW, false, true>), gd, bd, lds,
+                                   stream, a);
+                return true;
+            }
+        hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW, PREP, false>), gd, bd, lds, stream, a);
         return true;
     }
     return false;
 }
 
 template <int NT, typename XT, bool PREP>
-static hipError_t launch_mfma_p(int gpw, dim3 gd, dim3 bd, size_t lds, hipStream_t stream,
-                                const GemvArgs &a) {
+static hipError_t launch_mfma_p(int gpw, bool idle, dim3 gd, dim3 bd, size_t lds,
+                                hipStream_t stream, const GemvArgs &a) {
     bool launched = false;
     switch (gpw) {
-    case 1: launched = launch_mfma_g<NT, XT, 1, PREP>(gd, bd, lds, stream, a); break;
-    case 2: launched = launch_mfma_g<NT, XT, 2, PREP>(gd, bd, lds, stream, a); break;
-    case 4: launched = launch_mfma_g<NT, XT, 4, PREP>(gd, bd, lds, stream, a); break;
-    case 5: launched = launch_mfma_g<NT, XT, 5, PREP>(gd, bd, lds, stream, a); break;
-    case 8: if (!PREP) launched = launch_mfma_g<NT, XT, 8, PREP>(gd, bd, lds, stream, a); break;
-    case 10: if (!PREP) launched = launch_mfma_g<NT, XT, 10, PREP>(gd, bd, lds, stream, a); break;
-    case 16: if (!PREP) launched = launch_mfma_g<NT, XT, 16, PREP>(gd, bd, lds, stream, a); break;
+    case 1: launched = launch_mfma_g<NT, XT, 1, PREP>(idle, gd, bd, lds, stream, a); break;
+    case 2: launched = launch_mfma_g<NT, XT, 2, PREP>(idle, gd, bd, lds, stream, a); break;
+    case 4: launched = launch_mfma_g<NT, XT, 4, PREP>(idle, gd, bd, lds, stream, a); break;
+    case 5: launched = launch_mfma_g<NT, XT, 5, PREP>(idle, gd, bd, lds, stream, a); break;
+    case 8:
+        if (!PREP) launched = launch_mfma_g<NT, XT, 8, PREP>(idle, gd, bd, lds, stream, a);
+        break;
+    case 10:
+        if (!PREP) launched = launch_mfma_g<NT, XT, 10, PREP>(idle, gd, bd, lds, stream, a);
+        break;
+    case 16:
+        if (!PREP) launched = launch_mfma_g<NT, XT, 16, PREP>(idle, gd, bd, lds, stream, a);
+        break;
     default: break;
     }
     if (!launched) return hipErrorInvalidValue;   // the plan asked for no compiled instance
@@ -1202,7 +1224,7 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
     ReduceArgs ra = {};
     a.nrows = (int)nrows;
     ra.nrows = (int)nrows;
-    int waves = 1, gpw = 0;
+    int waves = 1, gpw = 0, min_waves = kMfmaMaxWaves;
     int64_t wg = 0, wsoff = 0;
     // by column: one unprepared row per pair; by expert: prepared chunks of kChunkRows rows
     const bool by_expert = route && route->chunk_expert;
@@ -1287,6 +1309,7 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         g.wg0 = (int)wg;
         wg += p.gx * p.slices;
         if (p.waves > waves) waves = p.waves;
+        if (p.waves < min_waves) min_waves = p.waves;
         if (p.gpw > gpw) gpw = p.gpw;
     }
     a.nlin = count;
@@ -1366,13 +1389,14 @@ static hipError_t launch_mfma_t(const GemvProblem *probs, int count, void *ws,
         }
     }
     const dim3 gd((unsigned)wg), bd(waves * 64);
+    const bool idle = count > 1 && min_waves < waves;
     hipError_t e;
     if constexpr (NT > 16)
-        e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
+        e = prep ? launch_mfma_p<NT, XT, true>(gpw, false, gd, bd, (size_t)lds, stream, a)
                  : hipErrorInvalidValue;
     else
-        e = prep ? launch_mfma_p<NT, XT, true>(gpw, gd, bd, (size_t)lds, stream, a)
-                 : launch_mfma_p<NT, XT, false>(gpw, gd, bd, (size_t)lds, stream, a);
+        e = prep ? launch_mfma_p<NT, XT, true>(gpw, false, gd, bd, (size_t)lds, stream, a)
+                 : launch_mfma_p<NT, XT, false>(gpw, idle, gd, bd, (size_t)lds, stream, a);
     if (e != hipSuccess) return e;
     if (ra.nlin > 0) {
         hipLaunchKernelGGL((gemv_mfma_reduce_kernel<NT>),

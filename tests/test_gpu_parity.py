@@ -135,6 +135,29 @@ def test_grouped_ragged_shapes_shared_x_and_k_split(n):
         assert ratio(yy, blk, x, out, in_) <= TOL_SMALL_N
 
 
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_grouped_linears_of_different_wave_counts(n):
+    """Linears whose plans take from one to eight waves share one launch (it
+    has the largest plan's waves, and the others' spare waves request
+    nothing), with K-split linears whose last slice leaves waves without
+    groups at 8 rows: every output as single calls and within the small-n
+    bound of the oracle."""
+    shapes = [(100, 5184), (48, 320), (200, 992), (33, 9728)]
+    xs = [synth.make_x(n, in_, seed=90 + i) for i, (_, in_) in enumerate(shapes)]
+    lins, blocks = [], []
+    for i, (out, in_) in enumerate(shapes):
+        blk = synth.make_blocks(out, in_, seed=95 + i)
+        p = packed_from_blocks(blk, out, in_)
+        lins.append((p, to_dev(xs[i]), torch.full((n, out), float("nan"), device=DEV), out, in_))
+        blocks.append(blk)
+    q4.matmul_grouped(lins, q4.F32, n)
+    torch.cuda.synchronize()
+    for i, ((p, _, y, out, in_), blk) in enumerate(zip(lins, blocks)):
+        yy = y.cpu().numpy()
+        assert np.array_equal(yy, run(p, xs[i], out)), (out, in_)
+        assert ratio(yy, blk, xs[i], out, in_) <= TOL_SMALL_N
+
+
 @pytest.mark.parametrize("n", [4, 5, 6, 12, 40])
 def test_grouped_matrices_of_both_sizes(n):
     """At 4 rows no matrix converts x by a pre-pass and the group shares one
