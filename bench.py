@@ -489,6 +489,22 @@ def mfma_loop_peak(torch, q4, reps=3):
     return round(best, 1)
 
 
+def dense_f16_library_ms(torch, o, i, n, steps, warmup, copies=4):
+    """Context for the prefill lines: the platform's dense binary16 GEMM
+    (torch.matmul, which calls the vendor BLAS library) on the same shape with
+    binary16 weights (four times the bytes, no decode), timed the same way."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(n, i, device="cuda", dtype=torch.float16, generator=g)
+    ws = [torch.randn(o, i, device="cuda", dtype=torch.float16, generator=g)
+          for _ in range(copies)]
+    ys = [torch.empty(n, o, device="cuda", dtype=torch.float16) for _ in range(copies)]
+    ms = time_steps(torch, lambda k, s: torch.matmul(x, ws[k % copies].t(), out=ys[k % copies]),
+                    steps, warmup)
+    del x, ws, ys
+    torch.cuda.empty_cache()
+    return ms
+
+
 def prefill_line(torch, q4, synth, kernel, steps, warmup):
     loop_peak = mfma_loop_peak(torch, q4)
     res = []
@@ -496,13 +512,17 @@ def prefill_line(torch, q4, synth, kernel, steps, warmup):
         c = Case(torch, q4, synth, o, i, 512, "f16", seed=li, copies=4, kernel=kernel)
         ms = timed(torch, q4, [c], steps, warmup)
         tfs = c.flops / (ms * 1e-3) / 1e12
+        flops = c.flops
+        del c
+        torch.cuda.empty_cache()
+        lib = dense_f16_library_ms(torch, o, i, 512, steps, warmup)
         res.append({"linear": f"{o}x{i}", "n": 512, "ms_per_step": round(ms, 5),
                     "TFLOP/s": round(tfs, 2), "frac_mfma_f16": round(tfs / F16_MFMA_PEAK_TFS, 4),
                     "mfma_loop_TFLOP/s": loop_peak, "frac_mfma_loop": round(tfs / loop_peak, 4),
                     "kernel": q4.KERNEL_NAMES[q4.q4_0_select_kernel(512, o, i, q4.F16)
-                                              if kernel == 0 else kernel]})
-        del c
-        torch.cuda.empty_cache()
+                                              if kernel == 0 else kernel],
+                    "dense_f16_library_ms": round(lib, 5),
+                    "dense_f16_library_TFLOP/s": round(flops / (lib * 1e-3) / 1e12, 2)})
     return res
 
 

@@ -65,8 +65,19 @@ constexpr int kGemmWaves = Q4_GEMM_WAVES;
 #endif
 static_assert(kGemmWaves == 4 || kGemmWaves == 8, "4 or 8 waves");
 constexpr int kThreads = kGemmWaves * 64;
-constexpr int kGemmMHalves = kGemmWaves / 4;           // waves along the activation rows
+// With eight waves, split the tile's weight rows four ways instead of its
+// activation rows two ways (each wave 128 activation rows x 32 weight rows
+// x half of K: no weight fragment is decoded twice, each A fragment feeds one
+// product instead of two).
+#ifndef Q4_GEMM_NSPLIT
+#define Q4_GEMM_NSPLIT 0
+#endif
+constexpr bool kNSplit = Q4_GEMM_NSPLIT && kGemmWaves == 8;
+constexpr int kGemmMHalves = kNSplit ? 1 : kGemmWaves / 4;   // waves along the activation rows
 constexpr int kGemmMSub = kGemmBM / 32 / kGemmMHalves;  // 32-row sub-tiles per wave
+constexpr int kNi = kNSplit ? 1 : 2;                     // 32-row weight sub-tiles per wave
+constexpr int kWaveCols = 32 * kNi;                      // weight rows per wave
+constexpr int kMfmaPerK = kGemmMSub * kNi;               // products per K-step
 constexpr int kStepBytes = kGemmBM * 128 * 2;  // one step's x tile: 32 KB
 constexpr int kPiecesPerThread = kStepBytes / 16 / kThreads;  // 8 or 4
 constexpr int kPiecesPerPart = (kPiecesPerThread + 2) / 3;    // x pieces in parts 0..2
@@ -155,7 +166,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     }
     const int mb = tile % a.nm;
     const int nb = tile / a.nm;
-    const int wn = wave & 1, wk = (wave >> 1) & 1, wm = wave >> 2;
+    const int wn = kNSplit ? (wave & 3) : (wave & 1);
+    const int wk = kNSplit ? (wave >> 2) & 1 : (wave >> 1) & 1;
+    const int wm = kNSplit ? 0 : wave >> 2;
     const int m0 = mb * kGemmBM;
     const int nsteps = gs1 - gs0;
     const XT *__restrict__ x = (const XT *)a.x;
@@ -259,22 +272,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // = tile 4 wn + 2 ni + c / 16, row c % 16; quarter 2h (+1: 256 bytes on),
     // blocks 2 wk, 2 wk + 1 (8 bytes); their scales (4 bytes) in the slot of
     // the wave that copied the tile (128 bytes per tile in the slot)
-    uint32_t woff[2], sgoff[2];
-    bool wvalid[2];
+    uint32_t woff[kNi], sgoff[kNi];
+    bool wvalid[kNi];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-        const int tl = 4 * wn + 2 * ni + (c >> 4);
+    for (int ni = 0; ni < kNi; ++ni) {
+        const int tl = (kWaveCols / 16) * wn + 2 * ni + (c >> 4);
         wvalid[ni] = t0 + tl < a.tiles;
         woff[ni] = kXBytes + tl * 1024 + ((2 * h) * 16 + (c & 15)) * 16 + 8 * wk;
         sgoff[ni] = kXBytes + kWBytes + (tl / kTilesPerWave) * 1024 + (tl % kTilesPerWave) * 128 +
                     (c & 15) * 8 + 4 * wk;
     }
 
-    f16x_t acc[kGemmMSub][2];
+    f16x_t acc[kGemmMSub][kNi];
 #pragma unroll
     for (int mi = 0; mi < kGemmMSub; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < kNi; ++ni)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
@@ -285,16 +298,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // The wave's part of a group: blocks 2wk, 2wk+1 = K-steps ks = 4wk+kq,
     // kq = 0..3.  K-step kq uses A from the stage and, per sub-tile, B = low
     // (kq even) or high (kq odd) nibbles of block 2wk + kq / 2.
-    u2_t w0[2], w1[2];                                       // code words of the step
-    uint32_t sc[2];                                          // their scales
-    uint32_t p01a[2], p23a[2], p01b[2], p23b[2];            // byte-spread words of a block
-    h2_t d2[2];
+    u2_t w0[kNi], w1[kNi];                                   // code words of the step
+    uint32_t sc[kNi];                                        // their scales
+    uint32_t p01a[kNi], p23a[kNi], p01b[kNi], p23b[kNi];    // byte-spread words of a block
+    h2_t d2[kNi];
     h8_t A[2][kGemmMSub];
-    h8_t B[2][2];
+    h8_t B[2][kNi];
     auto read_w = [&](int st) {
         const uint8_t *stage = lds + (st % kStages) * kStageBytes;
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < kNi; ++ni) {
             w0[ni] = *reinterpret_cast<const u2_t *>(stage + woff[ni]);
             w1[ni] = *reinterpret_cast<const u2_t *>(stage + woff[ni] + 256);
             sc[ni] = *reinterpret_cast<const uint32_t *>(stage + sgoff[ni]);
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     };
     auto spread = [&](int b) {                              // b: 0 or 1, block 2wk + b
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < kNi; ++ni) {
             const uint32_t u0 = w0[ni][b], u1 = w1[ni][b];
             p01a[ni] = __builtin_amdgcn_perm(u0, u0, 0x0C010C00u);
             p23a[ni] = __builtin_amdgcn_perm(u0, u0, 0x0C030C02u);
@@ -336,8 +349,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
         read_w(st);
         read_a(st, 0, A[0]);
         spread(0);
-        B[0][0] = frag(false, 0);
-        B[0][1] = frag(false, 1);
+#pragma unroll
+        for (int ni = 0; ni < kNi; ++ni) B[0][ni] = frag(false, ni);
     };
     // Interleave: one MFMA, then an LDS read and up to four VALU operations.
     // A wave issues in order and each MFMA holds the issue port while the
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     constexpr int kValuPerMfma = 16 / kGemmMSub;                 // 4 or 8
     auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < 2 * kGemmMSub; ++i) {
+        for (int i = 0; i < kMfmaPerK; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
             __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     };
     auto products = [&](int cur) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < kNi; ++ni)
 #pragma unroll
             for (int mi = 0; mi < kGemmMSub; ++mi)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][mi], B[cur][ni],
@@ -387,8 +400,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
             products(cur);
             read_a(st, kq + 1, A[cur ^ 1]);
             if (kq == 1) spread(1);
-            B[cur ^ 1][0] = frag(kq != 1, 0);
-            B[cur ^ 1][1] = frag(kq != 1, 1);
+#pragma unroll
+            for (int ni = 0; ni < kNi; ++ni) B[cur ^ 1][ni] = frag(kq != 1, ni);
             interleave();
         }
         if constexpr (NEXT) {
@@ -404,13 +417,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
             // travel, then the decode between the remaining products
             prep_first(st + 1);
             constexpr int kLead = kGemmMSub / 2;                    // products while words travel
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);      // DS read: words, scales
+            __builtin_amdgcn_sched_group_barrier(0x100, 3 * kNi, 0);  // DS read: words, scales
             __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);  // MFMA
 #pragma unroll
-            for (int i = 0; i < 2 * kGemmMSub - kLead; ++i) {
+            for (int i = 0; i < kMfmaPerK - kLead; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: A
-                __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * kGemmMSub - kLead), 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 24 * kNi / (kMfmaPerK - kLead), 0);  // VALU
             }
             __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -468,30 +481,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // 32 mi + 8 (v / 4) + 4 h + v % 4
     auto tix = [&](int mi, int ni, int v) {
         return (32 * (kGemmMSub * wm + mi) + 8 * (v >> 2) + 4 * h + (v & 3)) * kTileStride +
-               64 * wn + 32 * ni + c;
+               kWaveCols * wn + 32 * ni + c;
     };
     if (wk == 1) {
 #pragma unroll
         for (int mi = 0; mi < kGemmMSub; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < kNi; ++ni)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) ttile[tix(mi, ni, v)] = acc[mi][ni][v];
     }
     Q4_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     if (wk == 0) {
-        float other[kGemmMSub][2][16];
+        float other[kGemmMSub][kNi][16];
 #pragma unroll
         for (int mi = 0; mi < kGemmMSub; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < kNi; ++ni)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) other[mi][ni][v] = ttile[tix(mi, ni, v)];
 #pragma unroll
         for (int mi = 0; mi < kGemmMSub; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < kNi; ++ni)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) ttile[tix(mi, ni, v)] = acc[mi][ni][v] + other[mi][ni][v];
     }
