@@ -7,15 +7,20 @@
 // Instruction: v_mfma_f32_32x32x16_f16.  On gfx950 it retires twice the
 // flops per cycle of v_mfma_f32_16x16x32_f16, and each issue leaves about
 // four VALU slots free; the weight decode costs 14 VALU operations per 8
-// weights, so every decoded B fragment is reused by four MFMAs.
+// weights, so every decoded B fragment is reused by four MFMAs (the wave's
+// 128 activation rows).
 //
-// Tile: a workgroup computes 128 activation rows x 128 weight rows.  Wave
-// (wm, wn, wk) owns weight rows [64 wn, 64 wn + 64) of the tile, blocks
-// 2 wk, 2 wk + 1 of every 4-block group (128 k) of the workgroup's K slice
-// and, with eight waves, activation rows [64 wm, 64 wm + 64) (with four
-// waves all 128): 2 (or 4) x 2 accumulators of 32 x 32, so each A fragment
-// read from LDS feeds two MFMAs.  At the end the two K halves are summed
-// through LDS.
+// Tile: a workgroup computes 128 activation rows x 128 weight rows with
+// eight waves, two per SIMD.  Wave (wn, wk) owns weight rows [32 wn, 32 wn
+// + 32) of the tile, all 128 activation rows, and blocks 2 wk, 2 wk + 1 of
+// every 4-block group (128 k) of the workgroup's K slice: 4 accumulators of
+// 32 x 32.  No weight fragment is decoded twice in a workgroup, and while
+// one wave of a SIMD waits (on LDS, on the step barrier) the other's
+// products keep the matrix unit busy.  At the end the two K halves are
+// summed through LDS.  Build options keep the two earlier splits: four
+// waves, one per SIMD, each 128 activation rows x 64 weight rows (each A
+// fragment feeds two products), and eight waves splitting the activation
+// rows in two (64 x 64 per wave, every weight fragment decoded twice).
 //
 // Operands of one MFMA (K = 16, half a Q4_0 block):
 //   A: lane l = 32h + m holds activation row m of its 32-row sub-tile at
@@ -49,13 +54,14 @@ namespace q4 {
 
 constexpr int kGemmBM = 128;                 // activation rows per workgroup
 constexpr int kGemmBN = 128;                 // weight rows per workgroup
-// Waves per workgroup: 4 (one per SIMD, each wave 128 activation rows x 64
-// weight rows x half of K) or 8 (two per SIMD, each wave 64 x 64 x half of
-// K: the two activation halves decode the same weights, and while one wave
-// of a SIMD waits or decodes, the other's products keep the matrix unit
-// busy).
+// Waves per workgroup: 8 (two per SIMD) or 4 (one per SIMD, each wave 128
+// activation rows x 64 weight rows x half of K).  Measured on MI355X (graph
+// replay, three alternating runs): FFN-up 512 x 2560 . (9728 x 2560)^T
+// 39.0 us with eight waves splitting the weight rows against 40.1 us with
+// four, FFN-down 36.0 against 37.0 us; eight waves splitting the activation
+// rows instead took 43.0 / 40.2 us.
 #ifndef Q4_GEMM_WAVES
-#define Q4_GEMM_WAVES 4
+#define Q4_GEMM_WAVES 8
 #endif
 constexpr int kGemmWaves = Q4_GEMM_WAVES;
 // Partial tiles of the K slices stored with non-temporal stores (1) or plain
@@ -65,12 +71,10 @@ constexpr int kGemmWaves = Q4_GEMM_WAVES;
 #endif
 static_assert(kGemmWaves == 4 || kGemmWaves == 8, "4 or 8 waves");
 constexpr int kThreads = kGemmWaves * 64;
-// With eight waves, split the tile's weight rows four ways instead of its
-// activation rows two ways (each wave 128 activation rows x 32 weight rows
-// x half of K: no weight fragment is decoded twice, each A fragment feeds one
-// product instead of two).
+// With eight waves, split the tile's weight rows four ways (1) or its
+// activation rows two ways (0: each wave 64 x 64 x half of K).
 #ifndef Q4_GEMM_NSPLIT
-#define Q4_GEMM_NSPLIT 0
+#define Q4_GEMM_NSPLIT 1
 #endif
 constexpr bool kNSplit = Q4_GEMM_NSPLIT && kGemmWaves == 8;
 constexpr int kGemmMHalves = kNSplit ? 1 : kGemmWaves / 4;   // waves along the activation rows
@@ -268,8 +272,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     uint32_t aoff[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) aoff[ks] = c * 256 + 16 * ((2 * ks + h) ^ (c & 15));
-    // weight words of the lane in a stage: sub-tile ni = rows 64 wn + 32 ni + c
-    // = tile 4 wn + 2 ni + c / 16, row c % 16; quarter 2h (+1: 256 bytes on),
+    // weight words of the lane in a stage: sub-tile ni = rows W wn + 32 ni + c
+    // (W = kWaveCols weight rows per wave) = tile (W / 16) wn + 2 ni + c / 16,
+    // row c % 16; quarter 2h (+1: 256 bytes on),
     // blocks 2 wk, 2 wk + 1 (8 bytes); their scales (4 bytes) in the slot of
     // the wave that copied the tile (128 bytes per tile in the slot)
     uint32_t woff[kNi], sgoff[kNi];
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // Reads before writes: the compiler keeps LDS accesses that may alias in
     // program order, so interleaving them would serialize on LDS latency.
     float *ttile = reinterpret_cast<float *>(lds);           // 128 x 136 floats
-    // lane holds tile column 64 wn + 32 ni + c, tile rows
+    // lane holds tile column W wn + 32 ni + c, tile rows
     // 32 mi + 8 (v / 4) + 4 h + v % 4
     auto tix = [&](int mi, int ni, int v) {
         return (32 * (kGemmMSub * wm + mi) + 8 * (v >> 2) + 4 * h + (v & 3)) * kTileStride +
