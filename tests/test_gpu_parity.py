@@ -383,7 +383,10 @@ def test_mid_n_grouped_and_argmax():
 @pytest.mark.parametrize("n,out,in_", [(9, 100, 96), (64, 256, 128), (100, 300, 160),
                                        (130, 1000, 1056), (512, 1024, 1024),
                                        # few tiles, long K: the K range is split
-                                       (200, 300, 4096), (33, 130, 9728)])
+                                       (200, 300, 4096), (33, 130, 9728),
+                                       # 260 tiles: 256 whole and 4 split in K; ragged
+                                       # rows, columns and K
+                                       (400, 8200, 1056)])
 @pytest.mark.parametrize("xdt", [np.float16, np.float32], ids=["xf16", "xf32"])
 def test_gemm_parity_small(n, out, in_, xdt):
     blk = synth.make_blocks(out, in_, seed=n + out)
