@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="ffn_up_decode",
                     choices=["gemv_1024", "ffn_up_decode", "block_decode",
-                             "logit_head", "prefill", "launch_floor", "stream_read"])
+                             "logit_head", "prefill", "moe_routed", "launch_floor",
+                             "stream_read"])
     ap.add_argument("--n", type=int, default=None, help="rows of x (decode workloads)")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "gemv_dpp", "gemv_mfma", "gemm"])
@@ -397,15 +398,16 @@ def decode_line(torch, q4, synth, cal, name, linears, n, kernel, steps, warmup, 
 
 
 def routed_line(torch, q4, synth, cal, n, steps, warmup, n_exp=128, k=8, out=768, in_=2048,
-                hot=0):
+                hot=0, auto_only=False):
     """Routed (mixture-of-experts) decode, synthetic: n rows of x, each through
     k distinct experts drawn from n_exp experts of out x in (an expert FFN
     projection of a mid-size mixture model; the experts' shape is chosen, not
     taken from a page), or with hot > 0 from the same first `hot` experts
     (concentrated routing).  One q4_0_matmul_routed call per step, timed by
     column, by expert and as AUTO picks, and for n <= 4 against the same pairs
-    as n*k single-row q4_0_matmul calls.  GB/s counts the distinct experts'
-    Q4_0 bytes of a step."""
+    as n*k single-row q4_0_matmul calls (auto_only: the form AUTO picks alone,
+    for counter runs).  GB/s counts the distinct experts' Q4_0 bytes of a
+    step."""
     eb = q4.q4_0_blocks_bytes(out, in_)
     pb = q4.q4_0_packed_bytes(out, in_)
     copies = copies_for(n_exp * eb)
@@ -447,6 +449,9 @@ def routed_line(torch, q4, synth, cal, n, steps, warmup, n_exp=128, k=8, out=768
     auto = q4.q4_0_select_route(n, k, n_exp, out, in_)
     ms = {}
     for name, rk in (("by_column", q4.ROUTE_BY_COLUMN), ("by_expert", q4.ROUTE_BY_EXPERT)):
+        if auto_only and rk != auto:
+            ms[name] = None
+            continue
         try:
             ms[name] = time_steps(torch, routed(rk), steps, warmup)
         except q4.Q4Error:
@@ -465,7 +470,7 @@ def routed_line(torch, q4, synth, cal, n, steps, warmup, n_exp=128, k=8, out=768
            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
            "attainable_GB/s": att["GB/s"], "frac_attainable": round(gbs / att["GB/s"], 4),
            "rotation_copies": copies}
-    if n <= 4:
+    if n <= 4 and not auto_only:
         res["ms_single_calls"] = round(time_steps(torch, singles, steps, warmup), 5)
     del stacks, base
     torch.cuda.empty_cache()
@@ -584,6 +589,26 @@ def main():
     if args.workload in ("launch_floor", "stream_read"):
         print(json.dumps(calibration_main(torch, q4, cal, args)), flush=True)
         return
+    if args.workload == "moe_routed":
+        # the routed decode alone: the form AUTO picks, n rows (default 4)
+        n = args.n if args.n is not None else 4
+        line = routed_line(torch, q4, synth, cal, n, args.steps, args.warmup, auto_only=True)
+        roof = {"bound": "hbm", "achieved": line["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": line["frac_hbm"], "traffic": traffic_for(f"moe_routed_n{n}"),
+                "attainable_GB/s": line["attainable_GB/s"],
+                "frac_attainable": line["frac_attainable"]}
+        rec = {"metric": METRIC, "value": line["GB/s"], "unit": "GB/s", "n_gpus": 1,
+               "steps": timed_steps(args.steps), "steps_requested": args.steps,
+               "warmup": args.warmup, "ms_per_step": line["ms_per_step"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "f16", "data": "synthetic",
+               "config": {"workload": "moe_routed_decode", "n": n, "experts": line["experts"],
+                          "k": line["k"], "expert_shape": line["expert_shape"],
+                          "route": line["auto"]},
+               "roofline": roof, "extra": {"routed": [line], "calibration": cal.summary()},
+               "source_sha": source_hash()}
+        print(json.dumps(rec), flush=True)
+        return
     kernel = kernel_code(q4, args.kernel)
     wl = synth.WORKLOADS[args.workload]
     n = args.n if args.n is not None else wl.ns[0]
@@ -645,7 +670,11 @@ def main():
         floor = None if args.no_calibration else cal.launch_floor_us()
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_for(args.workload + (f"_n{n}" if n != 1 else "")),
+                "traffic": traffic_for(args.workload + ("_one_group" if args.one_group else "")
+                                       + ("_grouped" if args.grouped else "")
+                                       + ("_argmax" if args.argmax else "")
+                                       + ("_w4a8" if args.w4a8 else "")
+                                       + (f"_n{n}" if n != 1 else "")),
                 "algorithmic_bytes_per_launch": alg // calls,
                 "us_per_launch": round(ms / calls * 1e3, 4),
                 "us_per_launch_isolated": iso,
