@@ -52,7 +52,8 @@
 // several weight matrices, e.g. the Q, K and V projections of one input):
 // the workgroups of a launch are dealt to the linears in order, each linear
 // with its own plan; the launch's wave count is the largest plan's, and the
-// extra waves of a smaller plan have no groups.
+// extra waves of a smaller plan have no groups (in the IDLE instance they skip
+// the tiles and only join the reductions).
 #include "q4_0_device.h"
 #include "q4_0_internal.h"
 
@@ -166,6 +167,20 @@ constexpr int kFragHeader = 256;
 template <int NT> constexpr int red_tiles() { return NT > 32 ? 1 : (32 / NT < 2 ? 2 : 32 / NT); }
 // groups per wave a kernel instance holds in registers
 constexpr int kGpwSet[] = {1, 2, 4, 5, 8, 10, 16};
+
+// Rows the x staging lays a wave's lanes over: the power of two >= n.
+constexpr int stage_rows(int64_t n) { return n <= 1 ? 1 : (n <= 2 ? 2 : (n <= 4 ? 4 : (n <= 8 ? 8 : 16))); }
+
+// The value of lane l ^ 1 (resp. l ^ 2) within each quad of lanes (DPP
+// quad_perm, no LDS).
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
+                                                              0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
+                                                              0xF, 0xF, true));
+}
 
 // 2^e with e clamped to the float32 normal range.
 __device__ __forceinline__ float pow2f(int e) {
@@ -623,22 +638,26 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
 
     // ---- otherwise request this wave's range of x -----------------------------
     // item = (block bl, row t, quarter gq): the 8 values k = 32bl + 4gq +
-    // {0..3} and 32bl + 16 + 4gq + {0..3} of the wave's range.
-    constexpr int kItems = PREP ? 1 : (GPW * 16 * NT + 63) / 64;   // per lane
+    // {0..3} and 32bl + 16 + 4gq + {0..3} of the wave's range.  The rows are
+    // laid over kNTp, the power of two >= NT, so a lane's row t = (lane / 4)
+    // mod kNTp is the same for all its items (items of rows >= NT are empty).
+    constexpr int kNTp = stage_rows(NT);
+    constexpr int kItems = PREP ? 1 : (GPW * 16 * kNTp + 63) / 64;   // per lane
     static_assert(kItems <= kMaxStageItems, "x staging registers");
     const int kw0 = (gs0 + q0) * 128;                         // first k of the range
     const int kwn = ng == 0 ? 0 : (a.in - kw0 < ng * 128 ? a.in - kw0 : ng * 128);
-    const int items = ng * 16 * NT;
+    const int items = ng * 16 * kNTp;
+    const int trow = (lane >> 2) & (kNTp - 1);                // this lane's row
     float xv[kItems][8];
 #pragma unroll
     for (int ii = 0; ii < kItems; ++ii) {
         const int it = lane + ii * 64;
         const int gq = it & 3;
-        const int t = (it >> 2) % NT;
-        const int bl = (it >> 2) / NT;
+        const int t = trow;
+        const int bl = (it >> 2) / kNTp;
 #pragma unroll
         for (int k = 0; k < 8; ++k) xv[ii][k] = 0.0f;
-        if (!PREP && it < items && bl * 32 < kwn) {
+        if (!PREP && t < NT && it < items && bl * 32 < kwn) {
             const XT *p = x + (int64_t)t * a.in + kw0 + 32 * bl + 4 * gq;
             const float4 u = load_x4<XT>(p), v = load_x4<XT>(p + 16);
             xv[ii][0] = u.x; xv[ii][1] = u.y; xv[ii][2] = u.z; xv[ii][3] = u.w;
@@ -666,44 +685,33 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- stage the wave's x as A fragments -----------------------------------
-    // Each row's max |x| over the wave's range (a reduction across the wave's
-    // lanes, no LDS), then each lane scales its items, splits them into high
-    // and low binary16 parts and writes them as fragments into the wave's own
-    // LDS region.
-    float scale[NT];
+    // Each row's max |x| over the wave's range: the max over the lane's own
+    // items, then over the lanes of its row (those differing in the quarter
+    // bits and in the bits above the row's; no LDS for the quarter bits),
+    // then each lane scales its items, splits them into high and low binary16
+    // parts and writes them as fragments into the wave's own LDS region.
+    float scale_l = 1.0f;                                     // this lane's row's scale
     uint8_t *frag = smem + wave * (a.per * 4 * kBlockFrag);
     if constexpr (!PREP) {
-    float mloc[NT];
+    float m = 0.0f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) mloc[t] = 0.0f;
-#pragma unroll
-    for (int ii = 0; ii < kItems; ++ii) {
-        const int t = ((lane + ii * 64) >> 2) % NT;
-        float m = 0.0f;
+    for (int ii = 0; ii < kItems; ++ii)
 #pragma unroll
         for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(xv[ii][k]));
+    m = fmaxf(m, quad_xor1(m));
+    m = fmaxf(m, quad_xor2(m));
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) mloc[tt] = t == tt ? fmaxf(mloc[tt], m) : mloc[tt];
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        float m = mloc[t];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        scale[t] = row_scale(m);
-    }
+    for (int off = 4 * kNTp; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    scale_l = row_scale(m);
 #pragma unroll
     for (int ii = 0; ii < kItems; ++ii) {
         const int it = lane + ii * 64;
-        if (it < items) {
+        if (trow < NT && it < items) {
             const int gq = it & 3;
-            const int t = (it >> 2) % NT;
-            const int bl = (it >> 2) / NT;
-            float sc = scale[0];
-#pragma unroll
-            for (int tt = 1; tt < NT; ++tt) sc = t == tt ? scale[tt] : sc;
+            const int t = trow;
+            const int bl = (it >> 2) / kNTp;
             h8_t fh, fl;
-            split_fragment(xv[ii], sc, fh, fl);
+            split_fragment(xv[ii], scale_l, fh, fl);
             constexpr int kS = row_slots<NT>();
             *reinterpret_cast<h8_t *>(frag + ((bl * kS + t) * 4 + gq) * 16) = fh;
             if constexpr (kSplit)
@@ -743,9 +751,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                 }
             }
         } else {
-            float sc = 1.0f;
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) sc = row == tt ? scale[tt] : sc;
+            // the scale of D slot 4g+i's row, from a lane of that row
+            const float sc = __shfl(scale_l, 4 * (row < NT ? row : 0));
             inv[i] = inverse_pow2(sc);
         }
     }
@@ -1008,7 +1015,8 @@ static bool use_prep(int64_t n, int64_t out, int64_t in, bool gathered = false) 
 
 static int gpw_for(int64_t per, int64_t n, bool prep) {
     for (int v : kGpwSet)
-        if (v >= per && (prep || ((int64_t)v * 16 * n + 63) / 64 <= kMaxStageItems)) return v;
+        if (v >= per && (prep || ((int64_t)v * 16 * stage_rows(n) + 63) / 64 <= kMaxStageItems))
+            return v;
     return 0;
 }
 
@@ -1019,7 +1027,7 @@ static MfmaPlan mfma_plan(int64_t n, int64_t out, int64_t in, bool gathered = fa
     MfmaPlan p;
     // groups a wave may hold: the x it stages must fit its registers, or, when
     // prepared, the A fragments of its range
-    int64_t per_cap = prep ? prep_groups(n) : (kMaxStageItems * 64) / (16 * n);
+    int64_t per_cap = prep ? prep_groups(n) : (kMaxStageItems * 64) / (16 * stage_rows(n));
     if (per_cap > 16) per_cap = 16;
     if (per_cap < 1) per_cap = 1;     // n > 16: no plan can run (gemv_mfma_supports)
     // slices: as few as keep the slice within the waves' capacity and, when
@@ -1167,14 +1175,17 @@ bool gemv_mfma_group_uniform(const GemvProblem *probs, int count, int64_t n) {
 }
 
 // Launches the instance if it exists (its groups fit the registers); returns
-// whether it did.
-// (idle: some linear of the launch plans fewer waves than the launch has; only
-// unprepared launches have an IDLE instance, measured below)
+// whether it did.  idle: some linear of a grouped launch plans fewer waves
+// than the launch has, so the IDLE instance runs (unprepared launches up to 8
+// rows, where such groups arise: the block's seven linears in one call at
+// n = 1/2/4 took 17.5/19.6/21.2 us with it against 23.6/25.0/22.0 us, the
+// spare waves having requested their first group for every tile).
 template <int NT, typename XT, int GPW, bool PREP>
 static bool launch_mfma_g(bool idle, dim3 gd, dim3 bd, size_t lds, hipStream_t stream,
                           const GemvArgs &a) {
     if constexpr (PREP ? GPW <= prep_max_groups<NT>()
-                       : (NT <= 16 && ((int64_t)GPW * 16 * NT + 63) / 64 <= kMaxStageItems)) {
+                       : (NT <= 16 &&
+                          ((int64_t)GPW * 16 * stage_rows(NT) + 63) / 64 <= kMaxStageItems)) {
         if constexpr (!PREP && NT <= 8)
             if (idle) {
                 hipLaunchKernelGGL((gemv_mfma_kernel<NT, XT, GPW, false, true>), gd, bd, lds,
