@@ -25,6 +25,18 @@ __device__ __forceinline__ void dma16(const void *src, uint8_t *lds) {
                  : "memory", "m0");
 }
 
+// The same copy from a wave-uniform 64-bit base (scalar registers) plus a
+// 32-bit byte offset per lane: offsets computed once stay in registers across
+// a loop and only the base moves, so a copy costs no vector address
+// arithmetic.
+__device__ __forceinline__ void dma16_at(const void *base, uint32_t off, uint8_t *lds) {
+    const uint32_t lb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lb)
+                 : "memory", "m0");
+}
+
 static __device__ const u4_t kZeroPiece = {0u, 0u, 0u, 0u};
 
 // s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt left

@@ -212,6 +212,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     }
     const int ts = tw[((lane >> 3) & 1) % kTilesPerWave];
     const uint32_t soff_copy = (uint32_t)ts * a.g4 * kGroupScaleBytes + (lane & 7) * 16;
+    // byte offsets of the lane's code words from a group's first tile (the
+    // code stream is below 4 GiB: gemm_supports)
+    uint32_t woff_copy[kTilesPerWave];
+#pragma unroll
+    for (int u = 0; u < kTilesPerWave; ++u)
+        woff_copy[u] = (uint32_t)tw[u] * a.g4 * kGroupCodeBytes + lane * 16;
 
     // part p < 3 of step st's copies: x pieces P p .. P p + P - 1 (binary16
     // x only, P = kPiecesPerPart); code tile u of the wave at part 2 + u; the
@@ -226,24 +232,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
             for (int i = 0; i < kPiecesPerThread; ++i) {
                 if (part > 2 || i < kPiecesPerPart * part || i >= kPiecesPerPart * (part + 1))
                     continue;
-                const void *p = src + xoff[i];
                 if (partial) {
+                    // a group running past in: those lanes read a zero piece
                     const int r = 4 * kPiecesPerThread * wave + 4 * i + (lane >> 4);
                     const int q = (lane & 15) ^ (r & 15);
-                    p = j * 128 + 8 * q < a.in ? p : (const void *)&kZeroPiece;
+                    const void *p = j * 128 + 8 * q < a.in ? (const void *)(src + xoff[i])
+                                                           : (const void *)&kZeroPiece;
+                    dma16(p, xd + i * 1024);
+                } else {
+                    dma16_at(src, xoff[i], xd + i * 1024);
                 }
-                dma16(p, xd + i * 1024);
             }
         }
+        const uint8_t *cgroup = a.packed + a.code_base + (int64_t)j * kGroupCodeBytes;
 #pragma unroll
         for (int u = 0; u < kTilesPerWave; ++u)
             if (part == 2 + u)
-                dma16(a.packed + a.code_base + ((int64_t)tw[u] * a.g4 + j) * kGroupCodeBytes +
-                          lane * 16,
-                      stage + kXBytes + (kTilesPerWave * wave + u) * 1024);
+                dma16_at(cgroup, woff_copy[u], stage + kXBytes + (kTilesPerWave * wave + u) * 1024);
         if (part == 3)
-            dma16(a.packed + (int64_t)j * kGroupScaleBytes + soff_copy,
-                  stage + kXBytes + kWBytes + wave * 1024);
+            dma16_at(a.packed + (int64_t)j * kGroupScaleBytes, soff_copy,
+                     stage + kXBytes + kWBytes + wave * 1024);
     };
     X8 xp[kDma ? 1 : kPiecesPerThread];
     auto fetch = [&](int st) {                     // register path (float32 x): load
@@ -641,6 +649,8 @@ size_t gemm_workspace_bytes(int64_t n, int64_t out, int64_t in) {
 bool gemm_supports(int64_t n, int64_t out, int64_t in, int x_f16) {
     (void)x_f16;
     if (n < 1 || out < 1 || in < 32) return false;
+    // the copies address the code stream with 32-bit offsets from each group
+    if (Layout(out, in).total_bytes() >= ((int64_t)1 << 32)) return false;
     if (n * out > 0x7fffffff || n * in > ((int64_t)1 << 40)) return false;
     const GemmPlan p = gemm_plan(n, out, in);
     return p.wgs <= 0x7fffffff && gemm_workspace_bytes(n, out, in) <= kWorkspaceBytes;
