@@ -222,9 +222,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // part p < 3 of step st's copies: x pieces P p .. P p + P - 1 (binary16
     // x only, P = kPiecesPerPart); code tile u of the wave at part 2 + u; the
     // scales at part 3
-    auto fill = [&](int st, int part, bool partial) {
+    auto fill = [&](int st, auto sg, int part, bool partial) {
         const int j = gs0 + st;
-        uint8_t *stage = lds + (st % kStages) * kStageBytes;
+        uint8_t *stage = lds + sg * kStageBytes;
         if constexpr (kDma) {
             uint8_t *xd = stage + wave * (kPiecesPerThread * 1024);
             const uint8_t *src = (const uint8_t *)(xbase + j * 128);
@@ -267,9 +267,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
             }
         }
     };
-    auto park = [&](int st) {                      // register path: convert, write the stage
+    auto park = [&](auto sg) {                     // register path: convert, write the stage
         if constexpr (!kDma) {
-            uint8_t *xd = lds + (st % kStages) * kStageBytes + wave * (kPiecesPerThread * 1024) +
+            uint8_t *xd = lds + sg * kStageBytes + wave * (kPiecesPerThread * 1024) +
                           lane * 16;
 #pragma unroll
             for (int i = 0; i < kPiecesPerThread; ++i)
@@ -317,8 +317,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     h2_t d2[kNi];
     h8_t A[2][kGemmMSub];
     h8_t B[2][kNi];
-    auto read_w = [&](int st) {
-        const uint8_t *stage = lds + (st % kStages) * kStageBytes;
+    auto read_w = [&](auto sg) {
+        const uint8_t *stage = lds + sg * kStageBytes;
 #pragma unroll
         for (int ni = 0; ni < kNi; ++ni) {
             w0[ni] = *reinterpret_cast<const u2_t *>(stage + woff[ni]);
@@ -349,8 +349,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
         b[3] = as_u32((as_h2((p23b[ni] & mask) | magic) + off) * d2[ni]);
         return __builtin_bit_cast(h8_t, b);
     };
-    auto read_a = [&](int st, int kq, h8_t (&av)[kGemmMSub]) {
-        const uint8_t *stage = lds + (st % kStages) * kStageBytes;
+    auto read_a = [&](auto sg, int kq, h8_t (&av)[kGemmMSub]) {
+        const uint8_t *stage = lds + sg * kStageBytes;
 #pragma unroll
         for (int mi = 0; mi < kGemmMSub; ++mi)
             av[mi] = __builtin_bit_cast(
@@ -358,9 +358,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
                                                      (kGemmMSub * wm + mi) * 8192));
     };
     // operands of K-step 0 of step st into buffer 0
-    auto prep_first = [&](int st) {
-        read_w(st);
-        read_a(st, 0, A[0]);
+    auto prep_first = [&](auto sg) {
+        read_w(sg);
+        read_a(sg, 0, A[0]);
         spread(0);
 #pragma unroll
         for (int ni = 0; ni < kNi; ++ni) B[0][ni] = frag(false, ni);
@@ -398,10 +398,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // barrier also frees stage st for the copies of step st + 3.
     // REQ: step st + 2 exists; PART: its group runs past in; NEXT: st + 1
     // exists.
-    auto step = [&](int st, auto req_t, auto part_t, auto next_t) {
+    // sg: the LDS stage of step st (st mod kStages), a compile-time constant in
+    // the unrolled main loop, so every stage address folds into the LDS
+    // instructions' offsets.
+    auto step = [&](int st, auto sg, auto req_t, auto part_t, auto next_t) {
         constexpr bool REQ = decltype(req_t)::value;
         constexpr bool PART = decltype(part_t)::value;
         constexpr bool NEXT = decltype(next_t)::value;
+        const int sg_req = (sg + kStages - 1) % kStages;      // stage of step st + 2
+        const int sg_next = (sg + 1) % kStages;               // stage of step st + 1
         if constexpr (REQ && !kDma) fetch(st + kStages - 1);
         // The copies open each region: inline assembly is a scheduling
         // boundary, so copies placed between the products and the operand
@@ -409,9 +414,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int kq = 0; kq < 3; ++kq) {
             const int cur = kq & 1;
-            if (REQ) fill(st + kStages - 1, kq, PART);
+            if (REQ) fill(st + kStages - 1, sg_req, kq, PART);
             products(cur);
-            read_a(st, kq + 1, A[cur ^ 1]);
+            read_a(sg, kq + 1, A[cur ^ 1]);
             if (kq == 1) spread(1);
 #pragma unroll
             for (int ni = 0; ni < kNi; ++ni) B[cur ^ 1][ni] = frag(kq != 1, ni);
@@ -423,12 +428,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
             Q4_WAIT_LGKM0();
             __builtin_amdgcn_s_barrier();
         }
-        if (REQ) fill(st + kStages - 1, 3, PART);
+        if (REQ) fill(st + kStages - 1, sg_req, 3, PART);
         products(1);
         if constexpr (NEXT) {
             // next step's weight words first, two products while they
             // travel, then the decode between the remaining products
-            prep_first(st + 1);
+            prep_first(sg_next);
             constexpr int kLead = kGemmMSub / 2;                    // products while words travel
             __builtin_amdgcn_sched_group_barrier(0x100, 3 * kNi, 0);  // DS read: words, scales
             __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);  // MFMA
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
         } else {
             interleave();
         }
-        if constexpr (REQ && !kDma) park(st + kStages - 1);
+        if constexpr (REQ && !kDma) park(sg_req);
     };
 
     // ---- pipeline ------------------------------------------------------------
@@ -453,14 +458,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // of step st, converted and written at its end.
     for (int p = 0; p < kStages - 1 && p < nsteps; ++p) {
 #pragma unroll
-        for (int part = 0; part < 4; ++part) fill(p, part, (gs0 + p) * 128 + 128 > a.in);
+        for (int part = 0; part < 4; ++part) fill(p, p, part, (gs0 + p) * 128 + 128 > a.in);
         if constexpr (!kDma) { fetch(p); park(p); }
     }
     if (nsteps > 1) Q4_WAIT_VMCNT(kCopies);
     else Q4_WAIT_VMCNT(0);
     Q4_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
-    prep_first(0);
+    prep_first(std::integral_constant<int, 0>());
     // The steady state runs one variant of the step (the next-but-one step
     // exists and its group lies inside the row); the at most three last
     // steps are peeled, so the accumulators keep one register assignment
@@ -470,10 +475,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     const bool last_partial = gs1 * 128 > a.in;              // the slice's last group runs past in
     const int n_main = nsteps - (kStages - 1) - (last_partial ? 1 : 0);
     int st = 0;
-    for (; st < n_main; ++st) step(st, T(), F(), T());
-    if (last_partial && st == nsteps - kStages) step(st++, T(), T(), T());
-    if (st == nsteps - 2) step(st++, F(), F(), T());
-    if (st == nsteps - 1) step(st++, F(), F(), F());
+    static_assert(kStages == 3, "the main loop is unrolled over three stages");
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    for (; st + kStages <= n_main; st += kStages) {
+        step(st, S0(), T(), F(), T());
+        step(st + 1, S1(), T(), F(), T());
+        step(st + 2, S2(), T(), F(), T());
+    }
+    for (; st < n_main; ++st) step(st, st % kStages, T(), F(), T());
+    if (last_partial && st == nsteps - kStages) { step(st, st % kStages, T(), T(), T()); ++st; }
+    if (st == nsteps - 2) { step(st, st % kStages, F(), F(), T()); ++st; }
+    if (st == nsteps - 1) { step(st, st % kStages, F(), F(), F()); ++st; }
     Q4_WAIT_VMCNT(0);
     Q4_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
