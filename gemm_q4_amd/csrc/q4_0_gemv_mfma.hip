@@ -128,8 +128,12 @@ static int64_t target_wgs_small() {
 }
 constexpr int64_t kMfmaManyTiles = Q4_MFMA_MANY_TILES;
 constexpr int64_t kMfmaLdsBudget = Q4_MFMA_LDS_BUDGET;   // A fragments per workgroup
-// x items (8 values each) a lane holds while it stages: caps groups per wave x n
-constexpr int kMaxStageItems = 10;
+// x items (8 values each) a lane holds while it stages: caps groups per wave
+// x rows (the 16-row instance staging five groups holds 221 VGPRs, no spills)
+#ifndef Q4_MAX_STAGE_ITEMS
+#define Q4_MAX_STAGE_ITEMS 20
+#endif
+constexpr int kMaxStageItems = Q4_MAX_STAGE_ITEMS;
 // Activation rows from which x is converted once per launch by a pre-pass
 // (xprep_kernel) instead of by every workgroup.  Measured on MI355X (graph
 // replay, workgroups walking runs of tiles): FFN-up 9728 x 2560 at n = 4/5
@@ -141,10 +145,16 @@ constexpr int kMaxStageItems = 10;
 // 25.2/26.7 us with the pre-pass.  The 151936-row head at n = 4, two
 // workgroups per compute unit: 40.8 us converting per workgroup against 41.0
 // us with the pre-pass, and 45.2 against 46.7 us with the fused greedy pick.
-// So the pre-pass from 9 rows (where one binary16 part per row starts), and
-// from 5 rows for matrices of at least kMfmaManyTiles tiles.
+// With the staging that gives each lane one row and twenty staged items per
+// lane: FFN-up n = 12/16 11.18/11.34 us converting per workgroup against
+// 11.81/11.98 us with the pre-pass, the block as four grouped calls at
+// n = 16 49.2 against 51.7 us, in one grouped call at n = 12 26.0 against
+// 29.2 us; the head at n = 8 converting per workgroup 60.7 against 47.8 us.
+// So the pre-pass from 17 rows (where a second 16-row A group starts, whose
+// fragments a wave keeps in registers), and from 5 rows for matrices of at
+// least kMfmaManyTiles tiles.
 #ifndef Q4_MFMA_PREP_MIN_N
-#define Q4_MFMA_PREP_MIN_N 9
+#define Q4_MFMA_PREP_MIN_N 17
 #endif
 #ifndef Q4_MFMA_PREP_MIN_N_LARGE
 #define Q4_MFMA_PREP_MIN_N_LARGE 5
@@ -751,8 +761,9 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
                 }
             }
         } else {
-            // the scale of D slot 4g+i's row, from a lane of that row
-            const float sc = __shfl(scale_l, 4 * (row < NT ? row : 0));
+            // the scale of D slot 4g+i's row, from a lane of that row (with
+            // one row every lane holds it)
+            const float sc = kNTp == 1 ? scale_l : __shfl(scale_l, 4 * (row < NT ? row : 0));
             inv[i] = inverse_pow2(sc);
         }
     }

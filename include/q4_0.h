@@ -203,7 +203,7 @@ typedef struct q4_0_linear {
  * When q4_0_matmul would run the small-n MFMA kernel on every linear
  * (n <= 64 for the usual shapes) the group runs as one launch per 64 rows
  * (32 when a matrix has 4096 tiles or more; above 32 rows the linears must
- * agree), plus the activation pre-pass from 9 rows (from 5 for matrices of
+ * agree), plus the activation pre-pass from 17 rows (from 5 for matrices of
  * 4096 tiles or more) and a reduction launch if a linear splits K; otherwise
  * each linear runs as q4_0_matmul would, in array order, sharing the
  * workspace one after the other.  Every linear is checked before anything is

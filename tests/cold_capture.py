@@ -23,7 +23,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cases = [  # (name, n, out, in, x dtype): pre-pass, split K + reduction, prefill
-        ("decode_n12_prepass", 12, 9728, 2560, np.float32),
+        ("decode_n20_prepass", 20, 9728, 2560, np.float32),
         ("decode_n4_ksplit", 4, 2560, 9728, np.float32),
         ("prefill_512", 512, 2560, 9728, np.float16),
     ]

@@ -293,15 +293,16 @@ W16 = 1 << 42      # a fake, 256-byte aligned workspace address
 
 
 def test_workspace_sizes_of_the_workloads():
-    """The headline decode call needs no workspace, nor does FFN-up at 8
+    """The headline decode call needs no workspace, nor does FFN-up up to 16
     rows (one K slice, x converted per workgroup); the activation pre-pass
-    (from 9 rows), a split K range (the 9728-wide down projection), the
+    (from 17 rows), a split K range (the 9728-wide down projection), the
     split tiles of the prefill product and the greedy pick do."""
     mws = q4.q4_0_matmul_workspace_size
     assert mws(1, 9728, 2560) == 0
     assert mws(1, 151936, 2560) == 0
     assert mws(8, 9728, 2560) == 0
-    assert 0 < mws(9, 9728, 2560) <= q4.WORKSPACE_MAX
+    assert mws(16, 9728, 2560) == 0
+    assert 0 < mws(17, 9728, 2560) <= q4.WORKSPACE_MAX
     assert 0 < mws(8, 2560, 9728) <= q4.WORKSPACE_MAX
     assert 0 < mws(512, 9728, 2560, q4.F16) <= q4.WORKSPACE_MAX
     assert mws(1, 9728, 2560, q4.F32, q4.KERNEL_GEMV_DPP) == 0
@@ -309,8 +310,8 @@ def test_workspace_sizes_of_the_workloads():
     assert q4.q4_0_routed_workspace_size(64, 8, 128, 768, 2048, q4.ROUTE_BY_EXPERT) > 0
     assert q4.q4_0_w4a8_workspace_size(1, 9728, 2560) >= 0
     lin = [(A16, B16, C16, 4096, 2560), (A16 + (1 << 24), B16, C16 + (1 << 24), 1024, 2560)]
-    g = q4.q4_0_grouped_workspace_size(lin, q4.F32, 12)
-    assert g >= max(mws(12, 4096, 2560), mws(12, 1024, 2560)) > 0
+    g = q4.q4_0_grouped_workspace_size(lin, q4.F32, 20)
+    assert g >= max(mws(20, 4096, 2560), mws(20, 1024, 2560)) > 0
     # an invalid shape or selector is reported as the call would report it
     for bad, st in (((0, 10, 64), q4.ESHAPE), ((1, 10, 48), q4.ESHAPE)):
         with pytest.raises(q4.Q4Error) as e:

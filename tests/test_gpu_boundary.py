@@ -98,7 +98,7 @@ def test_graphs_captured_on_one_stream_replay_concurrently():
     the split-K decode and the activation pre-pass, which use the
     workspace): each replay gives its own eager result."""
     cases = []
-    for i, (n, out, in_) in enumerate([(4, 2560, 9728), (12, 9728, 2560)]):
+    for i, (n, out, in_) in enumerate([(4, 2560, 9728), (20, 9728, 2560)]):
         blk = synth.make_blocks(out, in_, seed=60 + i)
         p = packed_from_blocks(blk, out, in_)
         x = to_dev(synth.make_x(n, in_, seed=61 + i))

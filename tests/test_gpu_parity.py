@@ -158,15 +158,15 @@ def test_grouped_linears_of_different_wave_counts(n):
         assert ratio(yy, blk, xs[i], out, in_) <= TOL_SMALL_N
 
 
-@pytest.mark.parametrize("n", [4, 5, 6, 12, 40])
+@pytest.mark.parametrize("n", [4, 5, 6, 12, 20, 40])
 def test_grouped_matrices_of_both_sizes(n):
     """At 4 rows no matrix converts x by a pre-pass and the group shares one
-    launch; at 5 and 6 rows a matrix of 4096 tiles or more does and a small
-    one does not, so such a group runs as separate launches; from 9 rows both
-    use it and share one launch (checked at 12); at 40 rows the large matrices
-    take 32-row launches and the small one a 40-row launch, so the group runs
-    as separate launches again.  Every output as single calls and within the
-    small-n bound of the oracle."""
+    launch; from 5 to 16 rows a matrix of 4096 tiles or more does and a small
+    one does not, so such a group runs as separate launches (checked at 5, 6
+    and 12); from 17 rows both use it and share one launch (checked at 20);
+    at 40 rows the large matrices take 32-row launches and the small one a
+    40-row launch, so the group runs as separate launches again.  Every
+    output as single calls and within the small-n bound of the oracle."""
     shapes = [(65536 + 40, 64), (96, 64), (65536, 96)]
     xs = [synth.make_x(n, in_, seed=70 + i) for i, (_, in_) in enumerate(shapes)]
     lins, blocks = [], []

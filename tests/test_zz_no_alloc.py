@@ -36,8 +36,8 @@ def _both(blk, x_np, out, in_):
     # decode: a split K range (scratch used), then a smaller call that needs
     # less scratch
     ((8, 2560, 9728, np.float32), (4, 2560, 9728, np.float32)),
-    # the activation pre-pass (from 9 rows), then a smaller call
-    ((16, 9728, 2560, np.float32), (12, 1024, 2560, np.float32)),
+    # the activation pre-pass (from 17 rows), then a smaller call
+    ((24, 9728, 2560, np.float32), (20, 1024, 2560, np.float32)),
     # prefill: the split tiles' partial sums (15 MiB), then a smaller prefill
     ((512, 9728, 2560, np.float16), (100, 300, 4096, np.float16)),
 ])
