@@ -59,7 +59,7 @@ SMALL_SHAPES = [(1024, 1024), (37, 96), (300, 160), (16, 32), (1, 4128), (513, 2
 
 
 @pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("out,in_", SMALL_SHAPES)
 def test_small_n_parity(kernel, n, out, in_):
     if not _supported(kernel, n, out, in_):
@@ -227,6 +227,22 @@ def test_small_n_activation_range(kernel, xscale):
     x = (synth.make_x(n, in_, seed=13).astype(np.float64) * xscale).astype(np.float32)
     y = run(packed_from_blocks(blk, out, in_), x, out, kernel)
     assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
+
+
+@pytest.mark.parametrize("n", [3, 6, 8, 12, 16])
+def test_rows_of_very_different_scales(n):
+    """Each activation row takes its own power-of-two scale: rows from 1e-6 to
+    1e5 in one launch (a ragged K range), each within its own bound; a scale
+    taken from another row would overflow the large rows or lose the small
+    ones."""
+    out, in_ = 200, 4128
+    blk = synth.make_blocks(out, in_, seed=23)
+    x = synth.make_x(n, in_, seed=23).astype(np.float64)
+    x = (x * np.logspace(-6, 5, n)[:, None]).astype(np.float32)
+    y = run(packed_from_blocks(blk, out, in_), x, out, q4.KERNEL_GEMV_MFMA)
+    bound = TOL_SMALL_N if n <= 8 else BOUND_MID_N
+    for t in range(n):
+        assert ratio(y[t:t + 1], blk, x[t:t + 1], out, in_) <= bound, t
 
 
 @pytest.mark.parametrize("kernel", SMALL_N_KERNELS, ids=["dpp", "mfma"])
