@@ -84,6 +84,10 @@ def parse():
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the empty-launch and streaming-read legs (counter runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--isolated", action="store_true",
+                    help="profiling aid: only --steps launches of one linear (or of the "
+                         "empty launch), each followed by a synchronisation, so a kernel "
+                         "trace sees each dispatch alone")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -586,6 +590,13 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     cal = Calibration(torch, q4)
+    if args.workload == "launch_floor" and args.isolated:
+        g = Calibration.FLOOR_GRID
+        us = cal.isolated_us(lambda i, sh: q4.q4_0_stream_read(None, 0, cal.sink, g, sh),
+                             reps=args.steps)
+        print(json.dumps({"workload": "launch_floor", "isolated": True,
+                          "us_per_launch_isolated": us}), flush=True)
+        return
     if args.workload in ("launch_floor", "stream_read"):
         print(json.dumps(calibration_main(torch, q4, cal, args)), flush=True)
         return
@@ -631,6 +642,16 @@ def main():
         copies = copies_for(total_w)
         cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies, kernel=kernel)
                  for k, (o, i) in enumerate(linears)]
+        if args.isolated:
+            c = cases[0]
+            ncp = len(c.packed)
+            us = cal.isolated_us(lambda i, sh: q4.q4_0_matmul_ex(
+                c.packed[i % ncp], c.xs[i % len(c.xs)], c.xcode, c.y, c.n, c.out, c.in_,
+                c.kernel, c.ws, c.ws_need, sh), reps=args.steps)
+            print(json.dumps({"workload": args.workload, "n": n, "isolated": True,
+                              "linear": f"{c.out}x{c.in_}", "us_per_launch_isolated": us,
+                              "source_sha": source_hash()}), flush=True)
+            return
         groups = None
         names = [l.name for l in wl.linears]
         if args.workload == "block_decode" and args.grouped:
