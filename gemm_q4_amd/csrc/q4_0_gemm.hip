@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     // The K half wk = 1 writes its sums into a row-major tile in LDS (row
     // stride 136 floats: the two row groups of a write instruction land in
     // disjoint banks); wk = 0 reads them all, adds its own and writes the
-    // tile back; then all four waves store whole rows, 16 bytes per lane.
+    // tile back; then all the waves store whole rows, 16 bytes per lane.
     // Reads before writes: the compiler keeps LDS accesses that may alias in
     // program order, so interleaving them would serialize on LDS latency.
     float *ttile = reinterpret_cast<float *>(lds);           // 128 x 136 floats
