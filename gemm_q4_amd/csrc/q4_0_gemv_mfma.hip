@@ -1,6 +1,6 @@
-// Small-n Q4_0 product on the matrix cores: y[n x out] = x . W^T for n <= 32
-// rows per launch, for one linear or for a group of linears that share n in
-// one launch.
+// Small-n Q4_0 product on the matrix cores: y[n x out] = x . W^T for up to
+// 64 rows per launch, for one linear or for a group of linears that share n
+// in one launch.
 //
 // Why MFMA for a memory-bound product: a vector-ALU dot costs about n + 1.25
 // VALU operations per weight, more than the ~3.9 per weight that 70% of HBM
@@ -27,8 +27,9 @@
 // From 9 rows (the band between decode and prefill) each row takes one slot
 // holding its scaled binary16 value, without a low part: the precision of the
 // prefill kernel, which rounds x to binary16 as well (2^-11 relative).  Above
-// 16 rows a second A operand holds rows 16..31 and each decoded B fragment
-// feeds both products, so the weights are still read once.
+// 16 rows further A operands hold rows 16..63 (up to four 16-row groups) and
+// each decoded B fragment feeds all their products, so the weights are still
+// read once.
 //
 // Work split.  A workgroup owns a run of 16-row tiles of one linear and one
 // of its S slices of K; its waves take contiguous runs of `per` <= GPW
@@ -84,7 +85,8 @@ namespace q4 {
 // it is split.  Measured on MI355X: 96 KB keeps the block's 2560 x 9728 down
 // projection (76 groups) in one K slice at n = 2 and in two at n = 4
 // (grouped block n = 2/4: 29.0/35.8 us against 30.0/37.2 us with 56 KB);
-// 144 KB changes nothing measured.
+// 128 or 144 KB change nothing measured (the block as four grouped calls at
+// n = 8: 40.4/40.6 us against 40.7 us).
 #ifndef Q4_MFMA_LDS_BUDGET
 #define Q4_MFMA_LDS_BUDGET (96 * 1024)
 #endif
