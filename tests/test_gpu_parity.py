@@ -199,7 +199,7 @@ def test_grouped_prefill_runs_each_linear_with_the_gemm():
         assert ratio(y.cpu().numpy(), blk, x, out, in_) <= TOL_GEMM
 
 
-@pytest.mark.parametrize("n", [1, 4])
+@pytest.mark.parametrize("n", [1, 4, 8])
 def test_logit_head_full(n):
     out, in_ = 151936, 2560
     blk = synth.make_blocks(out, in_, seed=0)
@@ -698,15 +698,18 @@ def test_routed_index_outside_the_stack_gives_nan_rows():
     assert ratio(yy[3:4], blks[2], x[1:2], out, in_) <= TOL_SMALL_N
 
 
-def test_routed_moe_full_size():
+@pytest.mark.parametrize("n", [4, 32])
+def test_routed_moe_full_size(n):
     """A synthetic mixture-of-experts up projection: 128 experts of 768 x 2048,
-    8 experts per row, 4 rows; every output of every pair against the
-    oracle."""
-    out, in_, n_exp, k, n = 768, 2048, 128, 8, 4
+    8 experts per row, 4 rows (AUTO takes the by-column form) and 32 rows
+    (by expert); every output of every pair against the oracle."""
+    out, in_, n_exp, k = 768, 2048, 128, 8
     blks, stack = _expert_stack(n_exp, out, in_, seed=90)
     x = synth.make_x(n, in_, seed=91)
     rng = np.random.default_rng(92)
     route = np.stack([rng.permutation(n_exp)[:k] for _ in range(n)]).astype(np.int32)
+    want = q4.ROUTE_BY_COLUMN if n == 4 else q4.ROUTE_BY_EXPERT
+    assert q4.q4_0_select_route(n, k, n_exp, out, in_) == want
     yy = q4.matmul_routed(stack, n_exp, to_dev(x), to_dev(route), out).cpu().numpy()
     for t in range(n):
         for j in range(k):
