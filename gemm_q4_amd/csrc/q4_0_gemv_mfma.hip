@@ -602,13 +602,23 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
         bi[t] = 0x7fffffff;
     }
 
-    // lane's A slot r: high part of row r (r < NT), low part of row r - 8
-    // (8 <= r < 8 + NT); above 8 rows, row r.  Lanes of unused slots read
-    // slot 0's fragment: a D row depends only on its own A row, and the rows
-    // of unused slots are never read, so their contents do not matter (they
-    // stay finite).
+    // Lane's A slot r.  One row: high part in slot 0, low part in slot 8.
+    // 2..8 rows (paired): row t's high and low parts in adjacent slots
+    // 4(t / kRpg) + 2(t % kRpg) + {0, 1}, so both of its D values sit in one
+    // lane's registers (kRpg rows per lane group: 1 up to 4 rows, else 2).
+    // Above 8 rows, row r.  Lanes of unused slots read slot 0's fragment: a
+    // D row depends only on its own A row, and the rows of unused slots are
+    // never read, so their contents do not matter (they stay finite).
     constexpr bool kSplit = split_rows<NT>();
-    const int jslot = r < NT ? r : ((kSplit && r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
+    constexpr bool kPair = kSplit && NT >= 2;
+    constexpr int kRpg = NT <= 4 ? 1 : 2;
+    int jslot;
+    if constexpr (kPair) {
+        const int u = (r & 3) >> 1, t = (r >> 2) * kRpg + u;
+        jslot = u < kRpg && t < NT ? ((r & 1) ? NT + t : t) : 0;
+    } else {
+        jslot = r < NT ? r : ((kSplit && r >= 8 && r < 8 + NT) ? NT + (r - 8) : 0);
+    }
     // above 16 rows further A groups hold rows 16 j + r, j = 1 .. kRG - 1
     // (prepared x only); each decoded weight fragment then feeds kRG products
     constexpr int kRG = (NT + 15) / 16;
@@ -738,13 +748,13 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     const uint8_t *afrag = frag + (jslot * 4 + g) * 16;
-    // D slots a lane can hold live: 4g+i for i < min(NT, 4)
-    constexpr int kLive = NT < 4 ? NT : 4;
-    // inverse scale of the row behind D slot 4g+i (slot m and m+8 are one row)
+    // D slots a lane can hold live: 4g+i for i < kLive
+    constexpr int kLive = kPair ? 2 * kRpg : (NT < 4 ? NT : 4);
+    // inverse scale of the row behind D slot 4g+i
     float inv[kLive], inv_x[kXG][kLive];
 #pragma unroll
     for (int i = 0; i < kLive; ++i) {
-        const int row = kSplit ? ((4 * g + i) & 7) : 4 * g + i;
+        const int row = kPair ? g * kRpg + (i >> 1) : (kSplit ? ((4 * g + i) & 7) : 4 * g + i);
 #pragma unroll
         for (int j = 0; j < kXG; ++j) inv_x[j][i] = 1.0f;
         if constexpr (PREP) {
@@ -823,18 +833,28 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const Gem
             }
             if (next) load_group(t + 1, q);
         }
-        // undo the activation scale, add low parts (slots 8..15, lanes 32..63)
-        // to high parts (slots 0..7, lanes 0..31)
-        float v[kLive];
+        // undo the activation scale (a power of two: the products are exact)
+        // and add each row's low part to its high part: paired, in the lane;
+        // one row, from lanes 32..63 (slot 8) to lanes 0..31 (slot 0)
+        if constexpr (kPair) {
 #pragma unroll
-        for (int i = 0; i < kLive; ++i) {
-            v[i] = acc[i] * inv[i];
-            if constexpr (kSplit) v[i] += __shfl_xor(v[i], 32);
-        }
-        if (!kSplit || g < 2) {
+            for (int u = 0; u < kRpg; ++u) {
+                const int row = g * kRpg + u;
+                const float v = acc[2 * u] * inv[2 * u] + acc[2 * u + 1] * inv[2 * u + 1];
+                if (row < NT) red[slot][wave][row][r] = v;
+            }
+        } else {
+            float v[kLive];
 #pragma unroll
-            for (int i = 0; i < kLive; ++i)
-                if (4 * g + i < NT) red[slot][wave][4 * g + i][r] = v[i];
+            for (int i = 0; i < kLive; ++i) {
+                v[i] = acc[i] * inv[i];
+                if constexpr (kSplit) v[i] += __shfl_xor(v[i], 32);
+            }
+            if (!kSplit || g < 2) {
+#pragma unroll
+                for (int i = 0; i < kLive; ++i)
+                    if (4 * g + i < NT) red[slot][wave][4 * g + i][r] = v[i];
+            }
         }
         if constexpr (kRG > 1) {
 #pragma unroll
