@@ -177,6 +177,20 @@ constexpr int kFragHeader = 256;
 // tiles whose per-wave partial sums are parked before a workgroup reduction
 // (16 KB of LDS whatever n is)
 template <int NT> constexpr int red_tiles() { return NT > 32 ? 1 : (32 / NT < 2 ? 2 : 32 / NT); }
+// Prepared launches above 16 rows use no dynamic LDS, and their register use
+// (210-246 VGPRs) already leaves one workgroup per compute unit, so their
+// parked sums may take 96 KB: 3 tiles at 64 rows, 6 at 32 rows, instead of 1
+// and 2.  Measured on MI355X (graph replay): FFN-up 9728 x 2560 at n = 32/48
+// 13.7/21.6 us against 13.9/22.4 us, the 151936-row head at 32 rows 88.0
+// against 91.3 us, the block as four grouped calls at n = 64 101.4 against
+// 104.9 us; 64 KB gave about half of that.
+constexpr int kPrepRedBytes = 96 * 1024;
+template <int NT, bool PREP> constexpr int red_tiles_for() {
+    return PREP && NT > 16 ? (kPrepRedBytes / (kMfmaMaxWaves * NT * 64) < 1
+                                  ? 1
+                                  : kPrepRedBytes / (kMfmaMaxWaves * NT * 64))
+                           : red_tiles<NT>();
+}
 // groups per wave a kernel instance holds in registers
 constexpr int kGpwSet[] = {1, 2, 4, 5, 8, 10, 16};
 
@@ -534,7 +548,7 @@ __global__ __launch_bounds__(kPrepThreads) void route_prep_kernel(
 template <int NT, typename XT, int GPW, bool PREP, bool IDLE>
 __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemv_mfma_kernel(const GemvArgs args) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int kRedTiles = red_tiles<NT>();
+    constexpr int kRedTiles = red_tiles_for<NT, PREP>();
     __shared__ float red[kRedTiles][kMfmaMaxWaves][NT][16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
