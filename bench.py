@@ -369,10 +369,11 @@ def traffic_for(workload):
 
 
 def decode_line(torch, q4, synth, cal, name, linears, n, kernel, steps, warmup, groups=None,
-                argmax=False, w4a8=False, launches=None):
+                argmax=False, w4a8=False, launches=None, names=None):
     """One decode configuration: ms per step, effective weight GB/s, and the
     fraction of 8 TB/s and of the measured single-launch read of the step's
-    weight bytes."""
+    weight bytes.  With `names` (one call per linear), each linear is also
+    timed alone on the same buffers: `per_linear` gives its us per call."""
     total_w = sum(q4.q4_0_blocks_bytes(o, i) for o, i in linears)
     copies = copies_for(total_w)
     cases = [Case(torch, q4, synth, o, i, n, "f32", seed=k, copies=copies, kernel=kernel)
@@ -398,6 +399,17 @@ def decode_line(torch, q4, synth, cal, name, linears, n, kernel, steps, warmup, 
            "rotation_copies": copies}
     del cases
     torch.cuda.empty_cache()
+    if names is not None and groups is None and not argmax and not w4a8:
+        # each linear alone, its own copies rotated over at least 1 GiB
+        per = {}
+        for k, (nm, (o, i)) in enumerate(zip(names, linears)):
+            c = Case(torch, q4, synth, o, i, n, "f32", seed=k,
+                     copies=copies_for(q4.q4_0_blocks_bytes(o, i)), kernel=kernel)
+            per[f"{nm} {o}x{i}"] = round(timed(torch, q4, [c], steps, warmup) * 1e3, 3)
+            del c
+            torch.cuda.empty_cache()
+        res["per_linear_us"] = per
+        res["per_linear_sum_us"] = round(sum(per.values()), 3)
     return res
 
 
@@ -727,7 +739,7 @@ def main():
             one = [list(range(len(blk)))]
             for nn in (1, 2, 4, 8):
                 extra["decode"].append(decode_line(torch, q4, synth, cal, "block_decode", blk,
-                                                   nn, kernel, 300, 30))
+                                                   nn, kernel, 300, 30, names=bnames))
                 if kernel == q4.KERNEL_AUTO:
                     extra["decode"].append(decode_line(torch, q4, synth, cal, "block_decode",
                                                        blk, nn, kernel, 300, 30,
