@@ -229,12 +229,13 @@ def test_small_n_activation_range(kernel, xscale):
     assert ratio(y, blk, x, out, in_) <= TOL_SMALL_N
 
 
-@pytest.mark.parametrize("n", [3, 6, 8, 12, 16])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 7, 8, 12, 16])
 def test_rows_of_very_different_scales(n):
     """Each activation row takes its own power-of-two scale: rows from 1e-6 to
     1e5 in one launch (a ragged K range), each within its own bound; a scale
     taken from another row would overflow the large rows or lose the small
-    ones."""
+    ones.  2 to 8 rows cover every filling of the paired slots (one or two
+    rows per lane group, the last group partly used)."""
     out, in_ = 200, 4128
     blk = synth.make_blocks(out, in_, seed=23)
     x = synth.make_x(n, in_, seed=23).astype(np.float64)
